@@ -1,0 +1,173 @@
+"""Benchmark of the VC-Attention hot path on one MI355X.
+
+One step = the whole path on one batch of synthetic video-DiT-shaped input already resident
+in HBM: k-means grouping + label sort (vc_vsmooth_group), K/V smoothing and E4M3 operands
+(vc_vsmooth_demean_quant) and the FP8 attention with ExpCast-FP8 (vc_attn_fwd).
+
+Prints one JSON line.  `value` is attention work 4*B*H*N^2*d per step over the whole step's
+time (grouping included on every step, the worst case); the attention kernel alone is also
+timed with HIP events on the launch stream and reported against the FP8 MFMA peak.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config video|medium|reuse|long]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, vendor figure
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "attn_fwd_video_traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def attn_flops(B, H, N, d):
+    return 4.0 * B * H * N * N * d
+
+
+def cpu_baseline(cfg, Q, K, V, perm0, rows=256):
+    """The oracle's emulated VC attention for `rows` query rows of head 0 (full N keys)."""
+    from oracle import attention as T
+    from oracle import formats as F
+    from oracle import vsmooth as S
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    Qh, Kh, Vh = (F.bf16_value_from_bits(x[0, 0]) for x in (Q, K, V))
+    sel = np.unique(np.linspace(0, cfg.N - 1, rows).round().astype(np.int64))
+    t0 = time.perf_counter()
+    qc, sQ = S.quantize_q(Qh)
+    kc, sK = S.quantize_k(Kh, perm0)
+    vq = S.quantize_v(Vh, perm0)
+    T.attention_tiled(F.e4m3_decode(qc), sQ, F.e4m3_decode(kc), sK, F.e4m3_decode(vq["codes"]),
+                      vq["mu_t"], vq["sV"], rows=sel)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * len(sel) * cfg.N * cfg.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"emulated VC attention (operand quantisation + tiled ExpCast recurrence) for "
+                      f"{len(sel)} query rows x {cfg.N} keys of one head, {dt:.1f} s; "
+                      f"value = 4*rows*N*d / time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="video")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-only-iters", type=int, default=0,
+                    help="extra back-to-back vc_attn_fwd launches timed alone (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import bit_attention_video_amd as vc
+    import synth
+
+    cfg = synth.get_config(args.config)
+    B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    log(f"generating {cfg.name}: B={B} H={H} N={N} d={d} k={cfg.k}")
+    t0 = time.perf_counter()
+    Q, K, V = synth.make_qkv(cfg)
+    log(f"generated in {time.perf_counter() - t0:.1f} s")
+    dev = "cuda:0"
+    to = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    Qd, Kd, Vd = to(Q), to(K), to(V)
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        if ev: ev[0].record()
+        g = vc.vc_vsmooth_group(Vd, cfg.k, cfg.iters)
+        if ev: ev[1].record()
+        ops = vc.vc_vsmooth_demean_quant(Kd, Vd, g["perm"])
+        if ev: ev[2].record()
+        O = vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"])
+        if ev: ev[3].record()
+        return g, ops, O
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        g, ops, O = step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    t_group = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    t_dq = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    t_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    log(f"step {ms_step:.2f} ms: group {t_group:.2f} ms, demean_quant {t_dq:.3f} ms, attn {t_attn:.2f} ms")
+    assert torch.isfinite(O.float()).all(), "non-finite attention output"
+
+    if args.attn_only_iters:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.attn_only_iters):
+            vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"], out=O)
+        e1.record()
+        torch.cuda.synchronize()
+        log(f"attn alone x{args.attn_only_iters}: {e0.elapsed_time(e1) / args.attn_only_iters:.3f} ms")
+
+    fl = attn_flops(B, H, N, d)
+    attn_tflops = fl / (t_attn * 1e-3) / 1e12
+    value = fl / (ms_step * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            tr = json.load(f)
+        if tr.get("config") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+    # V-Smooth cost relative to attention (the pages' schedule: 40 steps, grouping at steps 0, 4, 8,
+    # demeaning on the first 25% of steps; the reuse window: group once, demean each of 4 steps)
+    amort = {
+        "grouping_step": (t_group + t_dq) / t_attn,
+        "reuse_window_4": (t_group + 4 * t_dq) / (4 * t_attn),
+        "schedule_40_steps": (3 * t_group + 10 * t_dq) / (40 * t_attn),
+    }
+    dq_bytes = 10.0 * B * H * N * d          # K, V read twice (bf16), Kq and Rq written
+    out = {
+        "metric": "FP8 VC-attn fwd TFLOP/s at N=70K,H=40,d=128; % of FP8 MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} H={H} N={N} d={d}, full V-Smooth (k-means k={cfg.k}, "
+                               f"{cfg.iters} Lloyd iters, sort, demean/quantise) + ExpCast FP8 attention",
+                   "B": B, "H": H, "N": N, "d": d, "k": cfg.k, "iters": cfg.iters},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "k_attn_fwd", "avg_launch_ms": round(t_attn, 4)},
+        "attn_ms": round(t_attn, 4), "attn_tflops": round(attn_tflops, 2),
+        "group_ms": round(t_group, 4), "demean_quant_ms": round(t_dq, 4),
+        "demean_quant_gbs": round(dq_bytes / (t_dq * 1e-3) / 1e9, 1),
+        "vsmooth_over_attn": {k2: round(v2, 4) for k2, v2 in amort.items()},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        perm0 = np.random.default_rng(0).permutation(N)   # any permutation: the cost does not depend on it
+        out["cpu_baseline"] = cpu_baseline(cfg, Q, K, V, perm0)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

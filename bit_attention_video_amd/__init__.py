@@ -1,0 +1,254 @@
+"""VC-Attention hot path on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libvcattn.so, whose C ABI is declared in include/vc_attn.h.
+This module only marshals arguments: it checks dtypes, shapes and devices of torch
+tensors, allocates outputs and workspaces with torch, and passes raw device pointers and
+torch's current HIP stream to the library.  Every step of the method runs in the HIP
+kernels; there is no CPU or PyTorch fallback, and a missing library is an error.
+
+Entry points (same names as the C ABI):
+  vc_vsmooth_group         k-means grouping + stable label sort (Sec. 3.2, Eq. 3)
+  vc_vsmooth_demean_quant  K smoothing, V block demeaning, E4M3 operands (Eq. 4, App. B)
+  vc_attn_fwd              FP8 attention with ExpCast-FP8 and mean restore (Eq. 1, 6, 7)
+  vc_test_*                single-stage hooks for testing
+plus vc_attention(Q, K, V, perm), which chains demean_quant and attn_fwd.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_attn_fwd",
+           "vc_attention", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
+           "vc_test_label_sort", "rq_tiled_to_natural", "rq_natural_to_tiled", "LIB_PATH",
+           "VC_ATTN_NO_MEAN", "VC_DQ_NO_DEMEAN", "STATUS"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvcattn.so")
+
+VC_ATTN_NO_MEAN = 0x1
+VC_DQ_NO_DEMEAN = 0x1
+STATUS = {"VC_OK": 0, "VC_ERR_NULL": -1, "VC_ERR_SHAPE": -2, "VC_ERR_K": -3, "VC_ERR_ITERS": -4,
+          "VC_ERR_WORKSPACE": -5, "VC_ERR_OVERFLOW": -6, "VC_ERR_FLAGS": -7, "VC_ERR_HIP": -8}
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_U = ctypes.c_uint
+_Z = ctypes.c_size_t
+_F = ctypes.c_float
+
+_SIGNATURES = {
+    "vc_strerror": (ctypes.c_char_p, [_I]),
+    "vc_last_hip_error": (_I, []),
+    "vc_group_workspace_size": (_Z, [_I, _I, _I, _I]),
+    "vc_vsmooth_group": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "vc_demean_quant_workspace_size": (_Z, [_I, _I, _I]),
+    "vc_vsmooth_demean_quant": (_I, [_P, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "vc_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
+    "vc_test_expcast": (_I, [_P, _P, _Z, _P]),
+    "vc_test_e4m3_encode": (_I, [_P, _P, _Z, _P]),
+    "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "vc_test_label_sort": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
+}
+
+_lib = None
+
+
+class VCError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib().vc_strerror(status).decode()
+        if status == STATUS["VC_ERR_HIP"]:
+            msg += f" (hipError_t {lib().vc_last_hip_error()})"
+        super().__init__(f"{where}: {msg} [{status}]")
+
+
+def lib() -> ctypes.CDLL:
+    """Load libvcattn.so (built in-tree by __graft_entry__.build()); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        raise VCError(rc, where)
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+
+
+def _bhnd(x: torch.Tensor, name: str):
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be [B, H, N, d]")
+    _need(x, name, torch.bfloat16)
+    return tuple(x.shape)
+
+
+def vc_vsmooth_group(V: torch.Tensor, k: int, iters: int, C_init: Optional[torch.Tensor] = None,
+                     objective: bool = True):
+    """k-means grouping of value tokens and pi = stable argsort(labels) (Sec. 3.2, Eq. 3)."""
+    B, H, N, d = _bhnd(V, "V")
+    dev = V.device
+    if C_init is not None:
+        _need(C_init, "C_init", torch.float32, (B, H, k, d))
+    C = torch.empty((B, H, k, d), dtype=torch.float32, device=dev)
+    labels = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    offsets = torch.empty((B, H, k + 1), dtype=torch.int32, device=dev)
+    J = torch.empty((B, H), dtype=torch.float64, device=dev) if objective else None
+    nws = lib().vc_group_workspace_size(B, H, N, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    _check(lib().vc_vsmooth_group(_ptr(V), B, H, N, d, k, iters, _ptr(C_init), _ptr(C), _ptr(labels),
+                                  _ptr(perm), _ptr(offsets), _ptr(J), _ptr(ws), nws, _stream()),
+           "vc_vsmooth_group")
+    return {"C": C, "labels": labels, "perm": perm, "offsets": offsets, "J": J}
+
+
+def vc_vsmooth_demean_quant(K: torch.Tensor, V: torch.Tensor, perm: Optional[torch.Tensor] = None,
+                            no_demean: bool = False):
+    """E4M3 operands of the VC path from bf16 K, V and pi (Sec. 3.2, Eq. 4; App. B)."""
+    B, H, N, d = _bhnd(K, "K")
+    _need(V, "V", torch.bfloat16, (B, H, N, d))
+    if perm is not None:
+        _need(perm, "perm", torch.int32, (B, H, N))
+    dev = K.device
+    T = N // 128 if N % 128 == 0 else 0
+    Kq = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    sK = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    Rq = torch.empty((B, H, T, d, 128), dtype=torch.uint8, device=dev)
+    mu = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    sV = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    nws = lib().vc_demean_quant_workspace_size(B, H, N)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    flags = VC_DQ_NO_DEMEAN if no_demean else 0
+    _check(lib().vc_vsmooth_demean_quant(_ptr(K), _ptr(V), _ptr(perm), B, H, N, d, flags, _ptr(Kq), _ptr(sK),
+                                         _ptr(Rq), _ptr(mu), _ptr(sV), _ptr(ws), nws, _stream()),
+           "vc_vsmooth_demean_quant")
+    return {"Kq": Kq, "sK": sK, "Rq": Rq, "mu": mu, "sV": sV}
+
+
+def vc_attn_fwd(Q: torch.Tensor, Kq: torch.Tensor, sK: torch.Tensor, Rq: torch.Tensor,
+                mu: Optional[torch.Tensor], sV: torch.Tensor, softmax_scale: float = 0.0,
+                no_mean: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """FP8 attention with ExpCast-FP8 and the online mean restore (Eq. 1, 6, 7)."""
+    B, H, N, d = _bhnd(Q, "Q")
+    T = N // 128 if N % 128 == 0 else 0
+    _need(Kq, "Kq", torch.uint8, (B, H, N, d))
+    _need(sK, "sK", torch.float32, (B, H, T))
+    _need(Rq, "Rq", torch.uint8, (B, H, T, d, 128))
+    if mu is not None or not no_mean:
+        _need(mu, "mu", torch.bfloat16, (B, H, T, d))
+    _need(sV, "sV", torch.float32, (B, H, d))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=Q.device)
+    else:
+        _need(out, "out", torch.bfloat16, (B, H, N, d))
+    flags = VC_ATTN_NO_MEAN if no_mean else 0
+    _check(lib().vc_attn_fwd(_ptr(Q), _ptr(Kq), _ptr(sK), _ptr(Rq), _ptr(mu), _ptr(sV), B, H, N, d,
+                             float(softmax_scale), flags, _ptr(out), _stream()), "vc_attn_fwd")
+    return out
+
+
+def vc_attention(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool = False):
+    """demean_quant then attn_fwd: O = attention(Q, K, V) on the VC path for a given pi."""
+    ops = vc_vsmooth_demean_quant(K, V, perm, no_demean=no_demean)
+    return vc_attn_fwd(Q, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"], softmax_scale,
+                       no_mean=no_demean)
+
+
+def vc_test_expcast(u: torch.Tensor) -> torch.Tensor:
+    _need(u, "u", torch.float32)
+    codes = torch.empty(u.shape, dtype=torch.uint8, device=u.device)
+    _check(lib().vc_test_expcast(_ptr(u), _ptr(codes), u.numel(), _stream()), "vc_test_expcast")
+    return codes
+
+
+def vc_test_e4m3_encode(x: torch.Tensor) -> torch.Tensor:
+    _need(x, "x", torch.float32)
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(lib().vc_test_e4m3_encode(_ptr(x), _ptr(codes), x.numel(), _stream()), "vc_test_e4m3_encode")
+    return codes
+
+
+def vc_test_kmeans_assign(V: torch.Tensor, C: torch.Tensor):
+    B, H, N, d = _bhnd(V, "V")
+    k = C.shape[2]
+    _need(C, "C", torch.float32, (B, H, k, d))
+    labels = torch.empty((B, H, N), dtype=torch.int32, device=V.device)
+    dist = torch.empty((B, H, N), dtype=torch.float32, device=V.device)
+    _check(lib().vc_test_kmeans_assign(_ptr(V), _ptr(C), B, H, N, d, k, _ptr(labels), _ptr(dist), _stream()),
+           "vc_test_kmeans_assign")
+    return labels, dist
+
+
+def vc_test_label_sort(labels: torch.Tensor, k: int):
+    if labels.dim() != 3:
+        raise ValueError("labels must be [B, H, N]")
+    _need(labels, "labels", torch.int32)
+    B, H, N = labels.shape
+    perm = torch.empty((B, H, N), dtype=torch.int32, device=labels.device)
+    offsets = torch.empty((B, H, k + 1), dtype=torch.int32, device=labels.device)
+    nws = lib().vc_group_workspace_size(B, H, N, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=labels.device)
+    _check(lib().vc_test_label_sort(_ptr(labels), B, H, N, k, _ptr(perm), _ptr(offsets), _ptr(ws), nws,
+                                    _stream()), "vc_test_label_sort")
+    return perm, offsets
+
+
+# ---- layout of the tile-transposed residual operand (include/vc_attn.h, Rq) ----
+
+def _key_of_slot() -> np.ndarray:
+    s = np.arange(128)
+    p, g, i = s // 64, (s // 32) % 2, s % 32
+    return 64 * p + 32 * (i // 16) + 8 * ((i % 16) // 4) + 4 * g + (i % 4)
+
+
+KEY_OF_SLOT = _key_of_slot()
+SLOT_OF_KEY = np.argsort(KEY_OF_SLOT)
+
+
+def rq_tiled_to_natural(Rq: torch.Tensor) -> torch.Tensor:
+    """[B,H,T,d,128 slots] -> [B,H,N,d] with rows in permuted token order (pure indexing)."""
+    B, H, T, d, _ = Rq.shape
+    nat = Rq.permute(0, 1, 2, 4, 3)                                   # [B,H,T,slot,d]
+    idx = torch.as_tensor(SLOT_OF_KEY, device=Rq.device)
+    return nat.index_select(3, idx).reshape(B, H, T * 128, d).contiguous()
+
+
+def rq_natural_to_tiled(R: torch.Tensor) -> torch.Tensor:
+    """[B,H,N,d] (permuted token order) -> [B,H,T,d,128 slots] (pure indexing)."""
+    B, H, N, d = R.shape
+    T = N // 128
+    t = R.reshape(B, H, T, 128, d)
+    idx = torch.as_tensor(KEY_OF_SLOT, device=R.device)
+    return t.index_select(3, idx).permute(0, 1, 2, 4, 3).contiguous()

@@ -1,0 +1,196 @@
+// C ABI of the VC-Attention library: argument validation (host only, before any HIP call),
+// workspace carving and kernel dispatch.  Contracts are documented in include/vc_attn.h.
+#include "vc_attn.h"
+#include "vc_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return VC_OK;
+  g_last_hip_error = (int)e;
+  return VC_ERR_HIP;
+}
+
+// Common shape checks. Returns VC_OK, an error, or 1 for an empty problem.
+int check_shape(int B, int H, int N, int d) {
+  if (B < 0 || H < 0 || N < 0) return VC_ERR_SHAPE;
+  if (d != VC_HEAD_DIM) return VC_ERR_SHAPE;
+  if (N % VC_BLOCK != 0) return VC_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return 1;
+  long long total = (long long)B * H * (long long)N * d;
+  if (total >= (1LL << 31)) return VC_ERR_OVERFLOW;
+  return VC_OK;
+}
+
+}  // namespace
+
+vc_group_ws vc_group_ws_layout(int BH, int N) {
+  vc_group_ws L;
+  size_t nblk = (size_t)(N + VC_SORT_TILE - 1) / VC_SORT_TILE;
+  size_t off = 0;
+  L.hist = off;  off = align256(off + (size_t)BH * nblk * 256 * sizeof(int32_t));
+  L.jpart = off; off = align256(off + (size_t)BH * ((size_t)(N + 255) / 256) * sizeof(double));
+  L.total = off;
+  return L;
+}
+
+vc_dq_ws vc_dq_ws_layout(int BH, int N) {
+  vc_dq_ws L;
+  size_t nchunk = (size_t)(N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  size_t off = 0;
+  L.kpart = off; off = align256(off + (size_t)BH * nchunk * 128 * sizeof(double));
+  L.kbar = off;  off = align256(off + (size_t)BH * 128 * sizeof(float));
+  L.mu = off;    off = align256(off + (size_t)BH * (size_t)(N / 128) * 128 * sizeof(float));
+  L.amax = off;  off = align256(off + (size_t)BH * 128 * sizeof(uint32_t));
+  L.total = off;
+  return L;
+}
+
+extern "C" {
+
+const char* vc_strerror(int status) {
+  switch (status) {
+    case VC_OK: return "ok";
+    case VC_ERR_NULL: return "required pointer is NULL";
+    case VC_ERR_SHAPE: return "bad shape (need d == 128, N % 128 == 0, sizes >= 0)";
+    case VC_ERR_K: return "k must be in [1, min(256, N)]";
+    case VC_ERR_ITERS: return "iters must be >= 1";
+    case VC_ERR_WORKSPACE: return "workspace too small";
+    case VC_ERR_OVERFLOW: return "B*H*N*d must be below 2^31";
+    case VC_ERR_FLAGS: return "unknown flag bits";
+    case VC_ERR_HIP: return "HIP call failed (see vc_last_hip_error)";
+    default: return "unknown status";
+  }
+}
+
+int vc_last_hip_error(void) { return g_last_hip_error; }
+
+size_t vc_group_workspace_size(int B, int H, int N, int k) {
+  (void)k;
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return vc_group_ws_layout(B * H, N).total;
+}
+
+size_t vc_demean_quant_workspace_size(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  return vc_dq_ws_layout(B * H, N).total;
+}
+
+int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int iters,
+                     const float* C_init, float* C_out, int32_t* labels, int32_t* perm,
+                     int32_t* offsets, double* objective, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!V || !C_out || !labels || !perm || !offsets || !ws) return VC_ERR_NULL;
+  if (k < 1 || k > VC_MAX_K || k > N) return VC_ERR_K;
+  if (iters < 1) return VC_ERR_ITERS;
+  int BH = B * H;
+  vc_group_ws L = vc_group_ws_layout(BH, N);
+  if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  int32_t* hist = (int32_t*)(w + L.hist);
+  double* jpart = (double*)(w + L.jpart);
+  hipError_t e = hipSuccess;
+  if (C_init) {
+    if (C_init != C_out)
+      e = hipMemcpyAsync(C_out, C_init, (size_t)BH * k * VC_HEAD_DIM * sizeof(float),
+                         hipMemcpyDeviceToDevice, stream);
+  } else {
+    e = vc_launch_kmeans_init(V, BH, N, k, C_out, stream);
+  }
+  if (e != hipSuccess) return hip_status(e);
+  for (int it = 0; it < iters; ++it) {
+    if ((e = vc_launch_kmeans_assign(V, C_out, BH, N, k, labels, nullptr, stream)) != hipSuccess)
+      return hip_status(e);
+    if ((e = vc_launch_label_sort(labels, BH, N, k, hist, perm, offsets, stream)) != hipSuccess)
+      return hip_status(e);
+    if ((e = vc_launch_kmeans_update(V, perm, offsets, BH, N, k, C_out, stream)) != hipSuccess)
+      return hip_status(e);
+  }
+  if (objective) {
+    if ((e = vc_launch_kmeans_objective(V, labels, C_out, BH, N, k, jpart, objective, stream)) !=
+        hipSuccess)
+      return hip_status(e);
+  }
+  return VC_OK;
+}
+
+int vc_vsmooth_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                            int B, int H, int N, int d, unsigned flags,
+                            uint8_t* Kq, float* sK, uint8_t* Rq, uint16_t* mu_out, float* sV,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!K || !V || !Kq || !sK || !Rq || !mu_out || !sV || !ws) return VC_ERR_NULL;
+  if (flags & ~VC_DQ_NO_DEMEAN) return VC_ERR_FLAGS;
+  int BH = B * H;
+  vc_dq_ws L = vc_dq_ws_layout(BH, N);
+  if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
+  return hip_status(vc_launch_demean_quant(K, V, perm, BH, N, flags, Kq, sK, Rq, mu_out, sV,
+                                           (char*)ws, L, stream));
+}
+
+int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uint8_t* Rq,
+                const uint16_t* mu, const float* sV, int B, int H, int N, int d,
+                float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!Q || !Kq || !sK || !Rq || !sV || !O) return VC_ERR_NULL;
+  if (!mu && !(flags & VC_ATTN_NO_MEAN)) return VC_ERR_NULL;
+  if (flags & ~VC_ATTN_NO_MEAN) return VC_ERR_FLAGS;
+  if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return VC_ERR_SHAPE;
+  // L = float32(8 log2(e) * scale), the scale taken in double (1/sqrt(d) when 0 is passed)
+  const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;
+  const float L = (float)(8.0 * 1.4426950408889634 * scale);
+  return hip_status(vc_launch_attn_fwd(Q, Kq, sK, Rq, mu, sV, B * H, N, L, flags, O, stream));
+}
+
+int vc_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t stream) {
+  if (n == 0) return VC_OK;
+  if (!u || !codes) return VC_ERR_NULL;
+  if (n >= (size_t(1) << 40)) return VC_ERR_OVERFLOW;
+  return hip_status(vc_launch_test_expcast(u, codes, n, stream));
+}
+
+int vc_test_e4m3_encode(const float* x, uint8_t* codes, size_t n, hipStream_t stream) {
+  if (n == 0) return VC_OK;
+  if (!x || !codes) return VC_ERR_NULL;
+  if (n >= (size_t(1) << 40)) return VC_ERR_OVERFLOW;
+  return hip_status(vc_launch_test_e4m3(x, codes, n, stream));
+}
+
+int vc_test_kmeans_assign(const uint16_t* V, const float* C, int B, int H, int N, int d, int k,
+                          int32_t* labels, float* mindist, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!V || !C || !labels) return VC_ERR_NULL;
+  if (k < 1 || k > VC_MAX_K || k > N) return VC_ERR_K;
+  return hip_status(vc_launch_kmeans_assign(V, C, B * H, N, k, labels, mindist, stream));
+}
+
+int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_t* perm,
+                       int32_t* offsets, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(B, H, N, VC_HEAD_DIM);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!labels || !perm || !offsets || !ws) return VC_ERR_NULL;
+  if (k < 1 || k > VC_MAX_K || k > N) return VC_ERR_K;
+  vc_group_ws L = vc_group_ws_layout(B * H, N);
+  if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
+  return hip_status(vc_launch_label_sort(labels, B * H, N, k, (int32_t*)((char*)ws + L.hist),
+                                         perm, offsets, stream));
+}
+
+}  // extern "C"

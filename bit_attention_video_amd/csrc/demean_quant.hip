@@ -1,0 +1,231 @@
+// K smoothing and V block demeaning with E4M3 quantisation, in permuted order
+// (VC-Attention Sec. 3.2 Eq. 3-4, "Block demeaning"; App. B, the K and V passes).
+//
+// Every statistic that feeds a code is reproducible bit for bit: sums of bf16 values are
+// taken in float64 (exact for the data here, hence order-free) and rounded to float32 once;
+// maxima are exact; x / s is one correctly rounded float32 division; E4M3 rounding is the
+// hardware's round-to-nearest-even conversion of a value already inside +-448.
+//
+// Passes (all grids are (blocks, b*h); 256 threads = 32 channel quads x 8 row groups):
+//   k_kstat_partial  float64 channel sums of K per 1024-row chunk
+//   k_kstat_final    kbar = float32(sum / N) in chunk order
+//   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = amax/448, codes
+//   k_vclear         zero the per-channel |R| maxima
+//   k_vpass1         per block of V[pi]: mu_j (float64 sum / 128), |R| maxima -> atomicMax
+//   k_vpass2         sV = amax/448; codes of R / sV into the tile-transposed PV operand order;
+//                    mu~ = bf16(mu / sV)
+#include "vc_common.h"
+#include "vc_internal.h"
+#include "vc_attn.h"
+
+__device__ __forceinline__ int dq_token(const int32_t* perm, int bh, int N, int pos) {
+  return perm ? perm[(size_t)bh * N + pos] : pos;
+}
+
+__device__ __forceinline__ void load4(const uint16_t* p, float* v) {
+  const uint2 raw = *(const uint2*)p;
+  v[0] = bf16_to_f32(raw.x & 0xFFFFu);
+  v[1] = bf16_to_f32(raw.x >> 16);
+  v[2] = bf16_to_f32(raw.y & 0xFFFFu);
+  v[3] = bf16_to_f32(raw.y >> 16);
+}
+
+__device__ __forceinline__ float block_max_256(float v, float* red4) {
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+}
+
+__global__ __launch_bounds__(256) void k_kstat_partial(const uint16_t* __restrict__ K, int N, int nchunk,
+                                                       double* __restrict__ kpart) {
+  __shared__ double part[8][VC_D];
+  const int bh = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, rg = t >> 5;
+  double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  const int r0 = ch * VC_KSTAT_CHUNK;
+  for (int i = rg; i < VC_KSTAT_CHUNK; i += 8) {
+    const int r = r0 + i;
+    if (r >= N) break;
+    float v[4];
+    load4(K + ((size_t)bh * N + r) * VC_D + 4 * q4, v);
+    a0 += v[0]; a1 += v[1]; a2 += v[2]; a3 += v[3];
+  }
+  part[rg][4 * q4 + 0] = a0;
+  part[rg][4 * q4 + 1] = a1;
+  part[rg][4 * q4 + 2] = a2;
+  part[rg][4 * q4 + 3] = a3;
+  __syncthreads();
+  if (t < VC_D) {
+    double s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += part[i][t];
+    kpart[((size_t)bh * nchunk + ch) * VC_D + t] = s;
+  }
+}
+
+__global__ __launch_bounds__(128) void k_kstat_final(const double* __restrict__ kpart, int N, int nchunk,
+                                                     float* __restrict__ kbar) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  double s = 0;
+  for (int c = 0; c < nchunk; ++c) s += kpart[((size_t)bh * nchunk + c) * VC_D + t];
+  kbar[(size_t)bh * VC_D + t] = (float)(s / (double)N);
+}
+
+__global__ __launch_bounds__(256) void k_kquant(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
+                                                const float* __restrict__ kbar, int N,
+                                                uint8_t* __restrict__ Kq, float* __restrict__ sK) {
+  __shared__ float red4[4];
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, rg = t >> 5;
+  const float4 kb = *(const float4*)(kbar + (size_t)bh * VC_D + 4 * q4);
+  float x[16][4];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 8 * i);
+    float v[4];
+    load4(K + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
+    x[i][0] = v[0] - kb.x;
+    x[i][1] = v[1] - kb.y;
+    x[i][2] = v[2] - kb.z;
+    x[i][3] = v[3] - kb.w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+  }
+  amax = block_max_256(amax, red4);
+  const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = j * VC_BLK + rg + 8 * i;
+    const uint32_t w = e4m3x4(x[i][0] / s, x[i][1] / s, x[i][2] / s, x[i][3] / s);
+    *(uint32_t*)(Kq + ((size_t)bh * N + r) * VC_D + 4 * q4) = w;
+  }
+  if (t == 0) sK[(size_t)bh * (N / VC_BLK) + j] = s;
+}
+
+__global__ __launch_bounds__(128) void k_vclear(uint32_t* __restrict__ amax) {
+  amax[(size_t)blockIdx.x * VC_D + threadIdx.x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_vpass1(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                int N, int demean, float* __restrict__ mu,
+                                                uint32_t* __restrict__ amax) {
+  __shared__ double part[8][VC_D];
+  __shared__ float mus[VC_D];
+  __shared__ float mx[8][VC_D];
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, rg = t >> 5;
+  float x[16][4];
+  double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 8 * i);
+    load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, x[i]);
+    a0 += x[i][0]; a1 += x[i][1]; a2 += x[i][2]; a3 += x[i][3];
+  }
+  part[rg][4 * q4 + 0] = a0;
+  part[rg][4 * q4 + 1] = a1;
+  part[rg][4 * q4 + 2] = a2;
+  part[rg][4 * q4 + 3] = a3;
+  __syncthreads();
+  if (t < VC_D) {
+    double s = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += part[i][t];
+    const float m = demean ? (float)(s / 128.0) : 0.0f;
+    mus[t] = m;
+    mu[((size_t)bh * (N / VC_BLK) + j) * VC_D + t] = m;
+  }
+  __syncthreads();
+  float m[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m[e] = 0.0f;
+  const float4 mv = *(const float4*)(mus + 4 * q4);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    m[0] = fmaxf(m[0], fabsf(x[i][0] - mv.x));
+    m[1] = fmaxf(m[1], fabsf(x[i][1] - mv.y));
+    m[2] = fmaxf(m[2], fabsf(x[i][2] - mv.z));
+    m[3] = fmaxf(m[3], fabsf(x[i][3] - mv.w));
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) mx[rg][4 * q4 + e] = m[e];
+  __syncthreads();
+  if (t < VC_D) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, mx[i][t]);
+    atomicMax(amax + (size_t)bh * VC_D + t, __float_as_uint(a));  // a >= 0: uint order = float order
+  }
+}
+
+// Position of permuted row r (0..127) of a tile in the PV operand order of vc_attn_fwd:
+// slot s = 64 p + 32 g + i holds key(s) = 64 p + 32 (i/16) + 8 ((i%16)/4) + 4 g + (i%4).
+__device__ __forceinline__ int pv_slot_of_key(int r) {
+  const int p = r >> 6, ih = (r >> 5) & 1, b8 = (r >> 3) & 3, g = (r >> 2) & 1, i4 = r & 3;
+  return 64 * p + 32 * g + 16 * ih + 4 * b8 + i4;
+}
+
+__global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                int N, const float* __restrict__ mu,
+                                                const uint32_t* __restrict__ amax,
+                                                uint8_t* __restrict__ Rq, uint16_t* __restrict__ mu_out,
+                                                float* __restrict__ sV) {
+  __shared__ float sc[VC_D];
+  __shared__ float mus[VC_D];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[VC_D * VC_BLK];
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, rg = t >> 5;
+  const int nt = N / VC_BLK;
+  if (t < VC_D) {
+    const float a = __uint_as_float(amax[(size_t)bh * VC_D + t]);
+    const float s = a == 0.0f ? 1.0f : a / 448.0f;
+    const float m = mu[((size_t)bh * nt + j) * VC_D + t];
+    sc[t] = s;
+    mus[t] = m;
+    mu_out[((size_t)bh * nt + j) * VC_D + t] = (uint16_t)f32_to_bf16_rne(m / s);
+    if (j == 0) sV[(size_t)bh * VC_D + t] = s;
+  }
+  __syncthreads();
+  const float4 s4 = *(const float4*)(sc + 4 * q4);
+  const float4 m4 = *(const float4*)(mus + 4 * q4);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = rg + 8 * i;
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + r);
+    float v[4];
+    load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
+    const uint32_t w = e4m3x4((v[0] - m4.x) / s4.x, (v[1] - m4.y) / s4.y,
+                              (v[2] - m4.z) / s4.z, (v[3] - m4.w) / s4.w);
+    const int slot = pv_slot_of_key(r);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[(4 * q4 + e) * VC_BLK + slot] = (uint8_t)(w >> (8 * e));
+  }
+  __syncthreads();
+  uint4* dst = (uint4*)(Rq + ((size_t)bh * nt + j) * (VC_D * VC_BLK));
+  const uint4* src = (const uint4*)tile;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dst[t + 256 * i] = src[t + 256 * i];
+}
+
+hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                  int BH, int N, unsigned flags, uint8_t* Kq, float* sK,
+                                  uint8_t* Rq, uint16_t* mu_out, float* sV, char* ws,
+                                  const vc_dq_ws& L, hipStream_t s) {
+  const int nchunk = (N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  const int nt = N / VC_BLK;
+  double* kpart = (double*)(ws + L.kpart);
+  float* kbar = (float*)(ws + L.kbar);
+  float* mu = (float*)(ws + L.mu);
+  uint32_t* amax = (uint32_t*)(ws + L.amax);
+  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
+  hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
+  hipLaunchKernelGGL(k_kquant, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
+  hipLaunchKernelGGL(k_vclear, dim3(BH), dim3(128), 0, s, amax);
+  hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(256), 0, s, V, perm, N,
+                     (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amax);
+  hipLaunchKernelGGL(k_vpass2, dim3(nt, BH), dim3(256), 0, s, V, perm, N, (const float*)mu,
+                     (const uint32_t*)amax, Rq, mu_out, sV);
+  return hipGetLastError();
+}

@@ -1,0 +1,211 @@
+// k-means grouping of value tokens (VC-Attention Sec. 3.2, "Value-guided permutation").
+//
+// Batch Lloyd per (b, h):
+//   init      c_c = V[floor((c + 1/2) N / k)] (float32)
+//   assign    z_t = argmin_c ||v_t - c_c||^2, ties to the lowest c.  The dot products v.c run
+//             on the bf16 matrix cores: v is exactly bf16, c is split into bf16 hi + lo parts
+//             (16 significant bits), two MFMAs accumulate in float32.  dist = ||c||^2 - 2 v.c;
+//             each lane keeps the best of its 16 centroids per block, one cross-lane exchange
+//             finishes the argmin.
+//   update    c_c = float32(sum of its rows / count), the sum in float64 in a fixed order over
+//             the rows of cluster c in sorted order (perm, offsets from the label sort); an
+//             empty cluster keeps its centroid.
+//   objective J = sum_t ||v_t - c_{z_t}||^2 in float64, fixed-order partials.
+#include "vc_common.h"
+#include "vc_internal.h"
+
+constexpr int KM_TOK_WG = 512;   // tokens per assign workgroup (4 waves x 4 groups x 32)
+constexpr int KM_ROW = 136;      // LDS row stride in bf16: 128 + 8 pad = 272 bytes
+
+__global__ __launch_bounds__(128) void k_kmeans_init(const uint16_t* __restrict__ V, int N, int k,
+                                                     float* __restrict__ C) {
+  const int c = blockIdx.x, bh = blockIdx.y, e = threadIdx.x;
+  const long long row = ((2LL * c + 1) * N) / (2LL * k);
+  C[((size_t)bh * k + c) * VC_D + e] = bf16_to_f32(V[((size_t)bh * N + row) * VC_D + e]);
+}
+
+__global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restrict__ V,
+                                                       const float* __restrict__ C, int N, int k,
+                                                       int kpad, int32_t* __restrict__ labels,
+                                                       float* __restrict__ mindist) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  uint16_t* chi = (uint16_t*)smem;                     // [kpad][KM_ROW]
+  uint16_t* clo = chi + (size_t)kpad * KM_ROW;         // [kpad][KM_ROW]
+  float* cn = (float*)(clo + (size_t)kpad * KM_ROW);   // [kpad]
+  const int bh = blockIdx.y, t = threadIdx.x;
+  const float* Cb = C + (size_t)bh * k * VC_D;
+
+  for (int i = t; i < kpad * VC_D; i += 256) {
+    const int c = i >> 7, e = i & 127;
+    const float x = c < k ? Cb[i] : 0.0f;
+    const uint32_t hi = f32_to_bf16_rne(x);
+    const uint32_t lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
+    chi[c * KM_ROW + e] = (uint16_t)hi;
+    clo[c * KM_ROW + e] = (uint16_t)lo;
+  }
+  for (int c = t; c < kpad; c += 256) {
+    float s = 0.0f;
+    if (c < k)
+      for (int e = 0; e < VC_D; ++e) s = fmaf(Cb[c * VC_D + e], Cb[c * VC_D + e], s);
+    cn[c] = c < k ? s : __builtin_inff();
+  }
+  __syncthreads();
+
+  const int w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
+  const int nblk = kpad >> 5;
+  for (int grp = 0; grp < KM_TOK_WG / 128; ++grp) {
+    const int tok = blockIdx.x * KM_TOK_WG + grp * 128 + w * 32 + q;
+    const bool valid = tok < N;
+    v8s vb[8];
+    float vn = 0.0f;
+    const uint16_t* vrow = V + ((size_t)bh * N + (valid ? tok : 0)) * VC_D;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      uint4 raw = valid ? *(const uint4*)(vrow + 16 * c + 8 * g) : make_uint4(0, 0, 0, 0);
+      vb[c] = __builtin_bit_cast(v8s, raw);
+      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = bf16_to_f32(wds[j] & 0xFFFFu), b = bf16_to_f32(wds[j] >> 16);
+        vn = fmaf(a, a, vn);
+        vn = fmaf(b, b, vn);
+      }
+    }
+    float best = __builtin_inff();
+    int bi = 0;
+    for (int cb = 0; cb < nblk; ++cb) {
+      v16f acc = {};
+      const uint16_t* hrow = chi + (cb * 32 + q) * KM_ROW + 8 * g;
+      const uint16_t* lrow = clo + (cb * 32 + q) * KM_ROW + 8 * g;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const v8s ah = *(const v8s*)(hrow + 16 * c);
+        const v8s al = *(const v8s*)(lrow + 16 * c);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah),
+                                                      __builtin_bit_cast(v8bf, vb[c]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al),
+                                                      __builtin_bit_cast(v8bf, vb[c]), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int ci = cb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        const float dist = fmaf(-2.0f, acc[i], cn[ci]);
+        if (dist < best) { best = dist; bi = ci; }
+      }
+    }
+    const float ob = __shfl_xor(best, 32, 64);
+    const int oi = __shfl_xor(bi, 32, 64);
+    if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    vn += __shfl_xor(vn, 32, 64);
+    if (valid && g == 0) {
+      labels[(size_t)bh * N + tok] = bi;
+      if (mindist) mindist[(size_t)bh * N + tok] = vn + best;
+    }
+  }
+}
+
+// Centroid update: one workgroup per (cluster, b*h); 16 row streams x 32 channel quads.
+__global__ __launch_bounds__(512) void k_kmeans_update(const uint16_t* __restrict__ V,
+                                                       const int32_t* __restrict__ perm,
+                                                       const int32_t* __restrict__ offsets,
+                                                       int N, int k, float* __restrict__ C) {
+  __shared__ double part[16][VC_D];
+  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int q4 = t & 31, st = t >> 5;
+  const int beg = offsets[(size_t)bh * (k + 1) + c], end = offsets[(size_t)bh * (k + 1) + c + 1];
+  if (end <= beg) return;  // empty cluster keeps its centroid (uniform branch)
+  const int32_t* pb = perm + (size_t)bh * N;
+  const uint16_t* Vb = V + (size_t)bh * N * VC_D + 4 * q4;
+  double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+#pragma unroll 4
+  for (int p = beg + st; p < end; p += 16) {
+    const int tok = pb[p];
+    const uint2 raw = *(const uint2*)(Vb + (size_t)tok * VC_D);
+    a0 += (double)bf16_to_f32(raw.x & 0xFFFFu);
+    a1 += (double)bf16_to_f32(raw.x >> 16);
+    a2 += (double)bf16_to_f32(raw.y & 0xFFFFu);
+    a3 += (double)bf16_to_f32(raw.y >> 16);
+  }
+  part[st][4 * q4 + 0] = a0;
+  part[st][4 * q4 + 1] = a1;
+  part[st][4 * q4 + 2] = a2;
+  part[st][4 * q4 + 3] = a3;
+  __syncthreads();
+  if (t < VC_D) {
+    double s = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += part[i][t];
+    C[((size_t)bh * k + c) * VC_D + t] = (float)(s / (double)(end - beg));
+  }
+}
+
+__global__ __launch_bounds__(256) void k_kmeans_objective(const uint16_t* __restrict__ V,
+                                                          const int32_t* __restrict__ labels,
+                                                          const float* __restrict__ C, int N, int k,
+                                                          double* __restrict__ jpart) {
+  __shared__ double red[256];
+  const int bh = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, tg = t >> 5;
+  double acc = 0;
+  for (int i = tg; i < 256; i += 8) {
+    const int tok = blk * 256 + i;
+    if (tok >= N) break;
+    const int z = labels[(size_t)bh * N + tok];
+    const uint2 raw = *(const uint2*)(V + ((size_t)bh * N + tok) * VC_D + 4 * q4);
+    const float4 c = *(const float4*)(C + ((size_t)bh * k + z) * VC_D + 4 * q4);
+    const double d0 = (double)bf16_to_f32(raw.x & 0xFFFFu) - c.x;
+    const double d1 = (double)bf16_to_f32(raw.x >> 16) - c.y;
+    const double d2 = (double)bf16_to_f32(raw.y & 0xFFFFu) - c.z;
+    const double d3 = (double)bf16_to_f32(raw.y >> 16) - c.w;
+    acc += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
+  }
+  red[t] = acc;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (t < off) red[t] += red[t + off];
+    __syncthreads();
+  }
+  if (t == 0) jpart[(size_t)bh * gridDim.x + blk] = red[0];
+}
+
+__global__ void k_kmeans_objective_final(const double* __restrict__ jpart, int nblk,
+                                         double* __restrict__ J) {
+  const int bh = blockIdx.x;
+  if (threadIdx.x == 0) {
+    double s = 0;
+    for (int i = 0; i < nblk; ++i) s += jpart[(size_t)bh * nblk + i];
+    J[bh] = s;
+  }
+}
+
+hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float* C, hipStream_t s) {
+  hipLaunchKernelGGL(k_kmeans_init, dim3(k, BH), dim3(128), 0, s, V, N, k, C);
+  return hipGetLastError();
+}
+
+hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
+                                   int32_t* labels, float* mindist, hipStream_t s) {
+  const int kpad = (k + 31) & ~31;
+  const size_t lds = (size_t)2 * kpad * KM_ROW * sizeof(uint16_t) + (size_t)kpad * sizeof(float);
+  hipError_t e = hipFuncSetAttribute((const void*)k_kmeans_assign,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int nblk = (N + KM_TOK_WG - 1) / KM_TOK_WG;
+  hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(256), lds, s, V, C, N, k, kpad, labels,
+                     mindist);
+  return hipGetLastError();
+}
+
+hipError_t vc_launch_kmeans_update(const uint16_t* V, const int32_t* perm, const int32_t* offsets,
+                                   int BH, int N, int k, float* C, hipStream_t s) {
+  hipLaunchKernelGGL(k_kmeans_update, dim3(k, BH), dim3(512), 0, s, V, perm, offsets, N, k, C);
+  return hipGetLastError();
+}
+
+hipError_t vc_launch_kmeans_objective(const uint16_t* V, const int32_t* labels, const float* C,
+                                      int BH, int N, int k, double* jpart, double* J, hipStream_t s) {
+  const int nblk = (N + 255) / 256;
+  hipLaunchKernelGGL(k_kmeans_objective, dim3(nblk, BH), dim3(256), 0, s, V, labels, C, N, k, jpart);
+  hipLaunchKernelGGL(k_kmeans_objective_final, dim3(BH), dim3(64), 0, s, (const double*)jpart, nblk, J);
+  return hipGetLastError();
+}

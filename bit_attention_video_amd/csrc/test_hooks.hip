@@ -1,0 +1,39 @@
+// Single-stage kernels exposed for testing: the ExpCast code (Sec. 3.3, Eq. 7) and the E4M3
+// quantiser, each with the exact instruction sequence the production kernels use.
+#include "vc_common.h"
+#include "vc_internal.h"
+
+// c(u) = clip(RNE(fma(8, u, C)), 0, 120), C = float32(120 + beta) = float32(119.65).
+// 8u is exact, so the FMA rounds once, as the Eq. 7 contract requires.  The byte comes from
+// the same saturating round-to-nearest-even conversion vc_attn_fwd uses; the integer is
+// clipped to 120 for u > 0 (outside the method's domain u <= 0, where t <= 119.65).
+__global__ void k_test_expcast(const float* __restrict__ u, uint8_t* __restrict__ codes, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) {
+    float t = __builtin_fmaf(8.0f, u[i], 119.65f);
+    uint32_t c = expcast_byte(t, 0, 0u) & 0xFFu;
+    codes[i] = (uint8_t)(c > 120u ? 120u : c);
+  }
+}
+
+__global__ void k_test_e4m3(const float* __restrict__ x, uint8_t* __restrict__ codes, size_t n) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < n; i += stride) codes[i] = (uint8_t)(e4m3x2(x[i], 0.0f) & 0xFFu);
+}
+
+static unsigned grid_for(size_t n) {
+  size_t g = (n + 255) / 256;
+  return (unsigned)(g > 65536 ? 65536 : g);
+}
+
+hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_expcast, dim3(grid_for(n)), dim3(256), 0, s, u, codes, n);
+  return hipGetLastError();
+}
+
+hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_e4m3, dim3(grid_for(n)), dim3(256), 0, s, x, codes, n);
+  return hipGetLastError();
+}

@@ -1,0 +1,72 @@
+// Device helpers shared by the VC-Attention kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define VC_D 128
+#define VC_BLK 128
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// bf16 bit pattern -> float32 (exact).
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// float32 -> bf16 bit pattern, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// E4M3 (OCP E4M3FN) codes of two float32 values, round to nearest even, saturating to
+// +-448: the hardware conversion rounds to nearest even and has no saturation, so the
+// operands are clamped first (|x| <= 448 keeps every finite input in range).
+// Returns the two codes in bits [0,16) of the result (x0 in byte 0).
+__device__ __forceinline__ uint32_t e4m3x2(float x0, float x1) {
+  x0 = fminf(fmaxf(x0, -448.0f), 448.0f);
+  x1 = fminf(fmaxf(x1, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false) & 0xFFFFu;
+}
+
+// Four E4M3 codes packed little-endian (x0 in byte 0).
+__device__ __forceinline__ uint32_t e4m3x4(float x0, float x1, float x2, float x3) {
+  x0 = fminf(fmaxf(x0, -448.0f), 448.0f);
+  x1 = fminf(fmaxf(x1, -448.0f), 448.0f);
+  x2 = fminf(fmaxf(x2, -448.0f), 448.0f);
+  x3 = fminf(fmaxf(x3, -448.0f), 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return (uint32_t)w;
+}
+
+// ExpCast rounding and clip (Eq. 7): byte `sel` of `old` <- clamp(RNE(t), 0, 255).
+// v_cvt_pk_u8_f32 rounds to nearest even and saturates to [0, 255] (NaN -> 0); the
+// callers guarantee t <= 120.5 or clip the integer to 120 themselves.
+__device__ __forceinline__ uint32_t expcast_byte(float t, uint32_t sel, uint32_t old) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(t, sel, old);
+}
+
+// Wave-wide reductions (wave64).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Block -> logical work item, XCD-aware: the hardware hands workgroup b to XCD b % 8, so
+// XCD x receives every 8th workgroup.  Remap so XCD x walks one contiguous range of the
+// logical order instead, so the CUs sharing one L2 work on neighbouring items at once.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t b, uint32_t G) {
+  const uint32_t X = 8;
+  uint32_t x = b % X, i = b / X;
+  uint32_t q = G / X, r = G % X;
+  uint32_t start = x * q + (x < r ? x : r);
+  return start + i;
+}

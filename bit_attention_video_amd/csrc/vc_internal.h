@@ -1,0 +1,51 @@
+// Host-side launchers of the VC-Attention kernels (internal; the public ABI is vc_attn.h).
+// Each launcher enqueues its kernels on `stream` and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+// Workspace layout of the grouping call (byte offsets from ws, each 256-byte aligned).
+struct vc_group_ws {
+  size_t hist;      // int32 [BH][nblk][256] per-block label histograms, then scatter bases
+  size_t jpart;     // float64 [BH][N/256] objective partial sums
+  size_t total;
+};
+vc_group_ws vc_group_ws_layout(int BH, int N);
+
+// Workspace layout of the demean/quantise call.
+struct vc_dq_ws {
+  size_t kpart;     // float64 [BH][nchunk][128] key channel partial sums
+  size_t kbar;      // float32 [BH][128] key channel means
+  size_t mu;        // float32 [BH][N/128][128] block means
+  size_t amax;      // uint32 [BH][128] residual |R| maxima (float bits)
+  size_t total;
+};
+vc_dq_ws vc_dq_ws_layout(int BH, int N);
+
+constexpr int VC_SORT_TILE = 1024;   // tokens per sort workgroup
+constexpr int VC_KSTAT_CHUNK = 1024; // rows per key-mean partial
+
+hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t s);
+hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s);
+
+hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float* C, hipStream_t s);
+hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
+                                   int32_t* labels, float* mindist, hipStream_t s);
+hipError_t vc_launch_kmeans_update(const uint16_t* V, const int32_t* perm, const int32_t* offsets,
+                                   int BH, int N, int k, float* C, hipStream_t s);
+hipError_t vc_launch_kmeans_objective(const uint16_t* V, const int32_t* labels, const float* C,
+                                      int BH, int N, int k, double* jpart, double* J, hipStream_t s);
+hipError_t vc_launch_label_sort(const int32_t* labels, int BH, int N, int k, int32_t* hist,
+                                int32_t* perm, int32_t* offsets, hipStream_t s);
+
+hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                  int BH, int N, unsigned flags, uint8_t* Kq, float* sK,
+                                  uint8_t* Rq, uint16_t* mu_out, float* sV, char* ws,
+                                  const vc_dq_ws& L, hipStream_t s);
+
+hipError_t vc_launch_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK,
+                              const uint8_t* Rq, const uint16_t* mu, const float* sV,
+                              int BH, int N, float L, unsigned flags, uint16_t* O,
+                              hipStream_t s);  // L = float32(8 log2(e) softmax_scale)

@@ -1,0 +1,179 @@
+/*
+ * vc_attn.h -- C ABI of the VC-Attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * Method: "VC-Attention: Value Smoothing and Softmax Casting for Low-bit Attention"
+ * (arXiv 2609.15810).  Non-causal FP8 attention forward with
+ *   V-Smooth   -- k-means grouping of value tokens, joint K/V permutation, 128-row
+ *                 block demeaning, E4M3 residuals, mean restored from the softmax
+ *                 row sum (Sec. 3.2, Eq. 3-6; App. B), and
+ *   ExpCast-FP8 -- the E4M3 probability byte written from the log-domain score by one
+ *                 FMA and one integer conversion (Sec. 3.3, Eq. 7).
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library never
+ *     allocates or frees device memory; scratch space comes in through `ws`.
+ *   - Layout is [B, H, N, d] row-major and contiguous unless stated otherwise.
+ *     bf16 tensors are passed as their 16-bit patterns (uint16_t).
+ *   - d must be 128 (VC_HEAD_DIM) and N a multiple of 128 (VC_BLOCK): the method's
+ *     hardware block is 128 rows (Sec. 3.2, Eq. 4) and padding is the caller's job
+ *     (App. B fuses it into the quantisers upstream).
+ *   - B * H * N * d must be below 2^31.
+ *   - B == 0, H == 0 or N == 0 is an empty problem: VC_OK, nothing touched.
+ *   - Every call validates its arguments on the host before any HIP call and
+ *     returns VC_OK (0) or a negative vc_status.  Work is enqueued asynchronously on
+ *     `stream`; nothing synchronises.  A failed launch returns VC_ERR_HIP and the
+ *     hipError_t is available from vc_last_hip_error() (per calling thread).
+ *   - Calls are re-entrant; there is no global state besides that error slot.
+ *   - Results are deterministic: no floating-point atomics, fixed reduction orders.
+ */
+#ifndef VC_ATTN_H
+#define VC_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum vc_status {
+  VC_OK = 0,
+  VC_ERR_NULL = -1,       /* a required pointer is NULL */
+  VC_ERR_SHAPE = -2,      /* negative size, d != 128 or N % 128 != 0 */
+  VC_ERR_K = -3,          /* k outside [1, min(256, N)] */
+  VC_ERR_ITERS = -4,      /* iters < 1 */
+  VC_ERR_WORKSPACE = -5,  /* ws_bytes below the size the matching *_workspace_size returns */
+  VC_ERR_OVERFLOW = -6,   /* B * H * N * d >= 2^31 */
+  VC_ERR_FLAGS = -7,      /* unknown flag bits */
+  VC_ERR_HIP = -8         /* a HIP call failed; see vc_last_hip_error() */
+};
+
+#define VC_HEAD_DIM 128
+#define VC_BLOCK 128
+#define VC_MAX_K 256
+
+/* vc_attn_fwd flags */
+#define VC_ATTN_NO_MEAN 0x1u     /* drop the r * mu term of Eq. 6 (the plain low-bit kernel) */
+/* vc_vsmooth_demean_quant flags */
+#define VC_DQ_NO_DEMEAN 0x1u     /* mu = 0: quantise V' itself (unsmoothed per-channel baseline) */
+
+/* Human-readable name of a vc_status. Never NULL. */
+const char* vc_strerror(int status);
+
+/* hipError_t of the last VC_ERR_HIP returned on the calling thread (0 if none). */
+int vc_last_hip_error(void);
+
+/* ------------------------------------------------------------------------------------------
+ * Grouping: k-means over value tokens and the label sort (Sec. 3.2, "Value-guided
+ * permutation", Eq. 3).
+ *
+ * Per (b, h), batch Lloyd k-means over the N value rows: `iters` rounds of
+ *   assign: z_t = argmin_c ||v_t - c_c||^2 (ties to the lowest c), then
+ *   update: c_c = mean of the rows labelled c (an empty cluster keeps its centroid).
+ * Start: C_init when non-NULL (warm start, [B,H,k,d] float32), else the rows
+ * floor((c + 1/2) N / k) of V.  Then pi = stable argsort(z) (ties keep token order).
+ *
+ *   V        in   bf16 [B,H,N,d]
+ *   C_init   in   float32 [B,H,k,d] or NULL
+ *   C_out    out  float32 [B,H,k,d]   centroids after the last update (may alias C_init)
+ *   labels   out  int32 [B,H,N]       labels of the last assignment
+ *   perm     out  int32 [B,H,N]       pi: perm[i] = token at sorted position i
+ *   offsets  out  int32 [B,H,k+1]     start of each cluster's run in pi; offsets[k] = N
+ *   objective out float64 [B,H]       J = sum_t ||v_t - c_{z_t}||^2 with the final labels and
+ *                                     centroids (may be NULL)
+ *   ws       scratch of at least vc_group_workspace_size(B,H,N,k) bytes, 256-byte aligned
+ * Distances are taken from bf16 x (bf16 hi + bf16 lo split of the float32 centroid) matrix
+ * products with float32 accumulation; centroid sums are float64 in a fixed order.
+ * -------------------------------------------------------------------------------------- */
+size_t vc_group_workspace_size(int B, int H, int N, int k);
+int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int iters,
+                     const float* C_init, float* C_out, int32_t* labels, int32_t* perm,
+                     int32_t* offsets, double* objective, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Smoothing and quantisation of K and V in permuted order (Sec. 3.2 Eq. 3-4; App. B).
+ *
+ * K path: kbar = float32(sum_t K[t] / N) (key channel mean, sum exact in float64);
+ *   K' = K[pi] - kbar (float32); per 128-row block j: sK[j] = amax|K'_j| / 448 (1 if 0);
+ *   Kq = E4M3_RNE(K' / sK[j]) in [B,H,N,d], rows in permuted order.
+ * V path: V' = V[pi]; mu_j = float32(sum of the 128 rows of block j / 128);
+ *   R = V' - mu_j (float32); sV[c] = amax_t |R[t,c]| / 448 over all N rows (1 if 0);
+ *   Rq = E4M3_RNE(R / sV[c]); mu_out[j][c] = bf16_RNE(mu_j[c] / sV[c]).
+ *   Flag VC_DQ_NO_DEMEAN sets mu = 0 (quantise V' itself).
+ * Every division is one correctly rounded float32 division; E4M3 is OCP E4M3FN with
+ * round-to-nearest-even (|x| <= 448 by construction).
+ *
+ *   K, V     in   bf16 [B,H,N,d]
+ *   perm     in   int32 [B,H,N] permutation of 0..N-1 per (b,h), or NULL for identity.
+ *                 Entries are not checked; values outside [0, N) are undefined behaviour.
+ *   Kq       out  E4M3 bytes [B,H,N,d]
+ *   sK       out  float32 [B,H,N/128]
+ *   Rq       out  E4M3 bytes, TILE-TRANSPOSED: [B,H,N/128][d][128 slots].  Within tile j,
+ *                 slot s of channel c holds residual code of permuted row 128 j + key(s) with
+ *                 key(s) = 64 p + 32 (i / 16) + 8 ((i % 16) / 4) + 4 g + (i % 4) for
+ *                 s = 64 p + 32 g + i (p, g in {0,1}, i in [0,32)).  This is the operand order
+ *                 of the PV matrix instruction in vc_attn_fwd.
+ *   mu_out   out  bf16 [B,H,N/128,d]  block means divided by sV (App. B)
+ *   sV       out  float32 [B,H,d]
+ *   ws       scratch of at least vc_demean_quant_workspace_size(B,H,N) bytes, 256-byte aligned
+ * -------------------------------------------------------------------------------------- */
+size_t vc_demean_quant_workspace_size(int B, int H, int N);
+int vc_vsmooth_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                            int B, int H, int N, int d, unsigned flags,
+                            uint8_t* Kq, float* sK, uint8_t* Rq, uint16_t* mu_out, float* sV,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * FP8 attention forward with ExpCast-FP8 and the online mean restore
+ * (Sec. 3.1 Eq. 1; Sec. 3.2 Eq. 6; Sec. 3.3 Eq. 7; App. B).
+ *
+ * Per (b,h) and query row i (original order; Q is never permuted), over key tiles
+ * j = 0 .. N/128-1 of the permuted keys:
+ *   Q block of 128 rows: sQ = amax/448 (1 if 0), Qq = E4M3_RNE(Q / sQ)
+ *   s = Qq . Kq_j (FP8 matrix instruction, float32 accumulate)
+ *   a = float32(float32(L * sQ) * sK[j]),  L = float32(8 log2(e) softmax_scale)
+ *   m' = max(m, a * max_k s);  b = float32(119.65 - m')
+ *   code = clip(RNE(fma(a, s, b)), 0, 120)  -- the E4M3 byte of P, 2^8 = row maximum
+ *   r = sum of decoded codes;  alpha = 2^((m - m')/8)
+ *   A = alpha A + P Rq_j + r mu_j;  l = alpha l + r     (mu term dropped by VC_ATTN_NO_MEAN)
+ *   O = bf16_RNE(sV * A / l)
+ *
+ *   Q        in   bf16 [B,H,N,d]
+ *   Kq, sK, Rq, mu, sV   in   as written by vc_vsmooth_demean_quant
+ *   softmax_scale        0 means 1/sqrt(d)
+ *   O        out  bf16 [B,H,N,d]
+ * -------------------------------------------------------------------------------------- */
+int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uint8_t* Rq,
+                const uint16_t* mu, const float* sV, int B, int H, int N, int d,
+                float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Test hooks: single stages of the path, exposed so each can be checked on its own.
+ * -------------------------------------------------------------------------------------- */
+
+/* ExpCast code of Eq. 7 for float32 u: clip(RNE(fma(8, u, 119.65f)), 0, 120); NaN -> 0.
+ * Same rounding and clip instruction sequence as vc_attn_fwd.  u, codes: device, n elements. */
+int vc_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t stream);
+
+/* E4M3 (OCP E4M3FN) round-to-nearest-even of float32 x, saturating to +-448, as the
+ * quantisers of vc_vsmooth_demean_quant and vc_attn_fwd do it. */
+int vc_test_e4m3_encode(const float* x, uint8_t* codes, size_t n, hipStream_t stream);
+
+/* One k-means assignment with given centroids C [B,H,k,d] float32 (the assign step of
+ * vc_vsmooth_group): labels int32 [B,H,N]; mindist float32 [B,H,N] (||v - c_z||^2 as the
+ * kernel computed it, may be NULL). */
+int vc_test_kmeans_assign(const uint16_t* V, const float* C, int B, int H, int N, int d, int k,
+                          int32_t* labels, float* mindist, hipStream_t stream);
+
+/* Stable counting sort of labels int32 [B,H,N] with values in [0,k): perm, offsets as in
+ * vc_vsmooth_group.  ws: at least vc_group_workspace_size(B,H,N,k) bytes. */
+int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_t* perm,
+                       int32_t* offsets, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VC_ATTN_H */

@@ -1,0 +1,128 @@
+"""The C ABI: the built library exports every entry point declared in include/vc_attn.h, and
+every argument error is reported on the host before any HIP call (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_attention_video_amd as vc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vc_attn.h")
+S = vc.STATUS
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails before any use
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int|size_t)\s+(vc_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = vc.lib()
+    names = _declared()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in vc._SIGNATURES, f"{n} has no binding"
+
+
+def test_header_statuses_match_binding():
+    text = open(HEADER).read()
+    for name, val in S.items():
+        m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
+        assert m and int(m.group(1)) == val, name
+
+
+def test_strerror():
+    lib = vc.lib()
+    for v in S.values():
+        assert lib.vc_strerror(v)
+    assert lib.vc_strerror(12345) == b"unknown status"
+
+
+def test_attn_fwd_argument_errors():
+    lib = vc.lib()
+    f = lib.vc_attn_fwd
+    P = [FAKE] * 6
+    assert f(*P, 1, 1, 128, 64, 0.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]        # d != 128
+    assert f(*P, 1, 1, 100, 128, 0.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]       # N % 128
+    assert f(*P, -1, 1, 128, 128, 0.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert f(*P, 1, 1, 1 << 24, 128, 0.0, 0, FAKE, None) == S["VC_ERR_OVERFLOW"]
+    assert f(None, *P[1:], 1, 1, 128, 128, 0.0, 0, FAKE, None) == S["VC_ERR_NULL"]
+    assert f(*P, 1, 1, 128, 128, 0.0, 0, None, None) == S["VC_ERR_NULL"]
+    # mu may be NULL only with VC_ATTN_NO_MEAN
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 128, 128, 0.0, 0, FAKE, None) == S["VC_ERR_NULL"]
+    assert f(*P, 1, 1, 128, 128, 0.0, 0x2, FAKE, None) == S["VC_ERR_FLAGS"]
+    assert f(*P, 1, 1, 128, 128, -1.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert f(*P, 1, 1, 128, 128, float("nan"), 0, FAKE, None) == S["VC_ERR_SHAPE"]
+    # empty problems are a no-op
+    assert f(None, None, None, None, None, None, 0, 4, 128, 128, 0.0, 0, None, None) == S["VC_OK"]
+    assert f(None, None, None, None, None, None, 1, 4, 0, 128, 0.0, 0, None, None) == S["VC_OK"]
+
+
+def test_group_argument_errors():
+    lib = vc.lib()
+    f = lib.vc_vsmooth_group
+    ws = lib.vc_group_workspace_size(1, 2, 1024, 8)
+    assert ws > 0
+    args = lambda N=1024, d=128, k=8, it=10, V=FAKE, nws=ws: (V, 1, 2, N, d, k, it, None, FAKE, FAKE, FAKE,
+                                                                FAKE, FAKE, FAKE, nws, None)
+    assert f(*args(d=127)) == S["VC_ERR_SHAPE"]
+    assert f(*args(N=1000)) == S["VC_ERR_SHAPE"]
+    assert f(*args(V=None)) == S["VC_ERR_NULL"]
+    assert f(*args(k=0)) == S["VC_ERR_K"]
+    assert f(*args(k=257)) == S["VC_ERR_K"]
+    assert f(*args(N=128, k=200)) == S["VC_ERR_K"]                             # k > N
+    assert f(*args(it=0)) == S["VC_ERR_ITERS"]
+    assert f(*args(nws=ws - 1)) == S["VC_ERR_WORKSPACE"]
+    assert f(*args(N=0)) == S["VC_OK"]
+
+
+def test_demean_quant_argument_errors():
+    lib = vc.lib()
+    f = lib.vc_vsmooth_demean_quant
+    ws = lib.vc_demean_quant_workspace_size(1, 2, 1024)
+    assert ws > 0
+    args = lambda N=1024, d=128, flags=0, K=FAKE, nws=ws: (K, FAKE, None, 1, 2, N, d, flags, FAKE, FAKE, FAKE,
+                                                            FAKE, FAKE, FAKE, nws, None)
+    assert f(*args(d=256)) == S["VC_ERR_SHAPE"]
+    assert f(*args(N=129)) == S["VC_ERR_SHAPE"]
+    assert f(*args(K=None)) == S["VC_ERR_NULL"]
+    assert f(*args(flags=0x4)) == S["VC_ERR_FLAGS"]
+    assert f(*args(nws=0)) == S["VC_ERR_WORKSPACE"]
+    assert f(*args(N=0)) == S["VC_OK"]
+
+
+def test_hook_argument_errors():
+    lib = vc.lib()
+    assert lib.vc_test_expcast(None, None, 0, None) == S["VC_OK"]
+    assert lib.vc_test_expcast(None, FAKE, 10, None) == S["VC_ERR_NULL"]
+    assert lib.vc_test_e4m3_encode(FAKE, None, 10, None) == S["VC_ERR_NULL"]
+    assert lib.vc_test_kmeans_assign(FAKE, FAKE, 1, 1, 256, 128, 300, FAKE, None, None) == S["VC_ERR_K"]
+    ws = lib.vc_group_workspace_size(1, 1, 256, 4)
+    assert lib.vc_test_label_sort(FAKE, 1, 1, 256, 4, FAKE, FAKE, FAKE, ws - 1, None) == S["VC_ERR_WORKSPACE"]
+
+
+def test_workspace_sizes_grow():
+    lib = vc.lib()
+    a = lib.vc_group_workspace_size(1, 8, 8192, 64)
+    b = lib.vc_group_workspace_size(1, 40, 70016, 128)
+    assert 0 < a < b
+    assert lib.vc_demean_quant_workspace_size(1, 8, 8192) < lib.vc_demean_quant_workspace_size(1, 40, 70016)
+    assert lib.vc_group_workspace_size(0, 8, 8192, 64) == 0
+
+
+def test_rq_layout_roundtrip_and_key_order():
+    import numpy as np
+    import torch
+    R = torch.randint(0, 256, (1, 2, 384, 128), dtype=torch.uint8)
+    T = vc.rq_natural_to_tiled(R)
+    assert T.shape == (1, 2, 3, 128, 128)
+    assert torch.equal(vc.rq_tiled_to_natural(T), R)
+    assert sorted(vc.KEY_OF_SLOT.tolist()) == list(range(128))
+    # slot s = 64p + 32g + i holds key 64p + 32(i/16) + 8((i%16)/4) + 4g + i%4
+    assert vc.KEY_OF_SLOT[0] == 0 and vc.KEY_OF_SLOT[1] == 1 and vc.KEY_OF_SLOT[4] == 8
+    assert vc.KEY_OF_SLOT[16] == 32 and vc.KEY_OF_SLOT[32] == 4 and vc.KEY_OF_SLOT[64] == 64
+    assert np.array_equal(T[0, 1, 2, 5, :].numpy(), R[0, 1, 256 + vc.KEY_OF_SLOT, 5].numpy())   # [.., c, s]
