@@ -72,7 +72,20 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only-iters", type=int, default=0,
                     help="extra back-to-back vc_attn_fwd launches timed alone (for profiling)")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calib_mib:
+        import torch
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)

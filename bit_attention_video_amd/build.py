@@ -22,6 +22,9 @@ ARCH = "gfx950"
 # Packed FP32 instructions are disabled for every HIP source (v_pk_*_f32 are never emitted).
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep matrix-instruction results in architectural VGPRs: the softmax reads every
+          # score with vector instructions, and AGPR copies would double that traffic
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-result"]
 
 

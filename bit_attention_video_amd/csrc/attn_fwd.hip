@@ -11,16 +11,29 @@
 //   O^T (d x queries)   += Rq_j^T (d x keys) . P^T (keys x queries)
 // In the 32x32 result layout lane (q = lane%32, g = lane/32) holds column q and rows
 // 8(i/4) + 4g + i%4 (i = 0..15), so every score, row statistic and output element of a
-// lane belongs to query q; the two lanes q and q+32 share a row and exchange one value.
+// lane belongs to query q; the lanes q and q+32 share a row and exchange one value.
 // The P bytes a lane produces are exactly its B-operand bytes for PV once the residual
 // tile is stored in the matching key order (vc_vsmooth_demean_quant's tile-transposed Rq).
 //
-// Per tile, per query row (Eq. 1 with the Fig. 2 / Eq. 7 folding, in units of 8 log2(e) S):
-//   a = float32(qa * sK_j), qa = float32(L * sQ), L = float32(8 log2(e) softmax_scale)
-//   m' = max(m, a * rowmax s);  b = float32(119.65 - m');  alpha = 2^((m - m')/8)
-//   code = clamp(RNE(fma(a, s, b)), 0, 255) by v_cvt_pk_u8_f32; fma(a,s,b) <= 119.65 + ulp,
-//          so this is Eq. 7's clip to [0, 120]; the byte is the E4M3 P element
-//   r = sum of decoded codes;  l = alpha l + r;  A = alpha A + r mu~_j (Eq. 6), then += P R
+// ExpCast inside the matrix unit.  The query block is quantised as E4M3(Q L / sQ) with
+// L = float32(8 log2(e) softmax_scale), and sQ, sK_j are powers of two (E8M0), so the scaled
+// FP8 instruction with block scales sK_j and sQ already returns a*s = 8 log2(e) S, the
+// score in Eq. 7's units.  Its accumulator input is b = 119.65 - m (the row maximum folded
+// into the constant, Fig. 2 caption), so it returns t = a*s + b and Eq. 7 is left with
+// Round and clip: one v_cvt_pk_u8_f32 per element (RNE, saturating; t <= 119.65 + ulp, so
+// the saturation at 0 is the clip and 120 is never exceeded).
+//
+// Running maximum (Eq. 1).  With t = a s + C - m, rowmax(t) - C = a*max(s) - m, so a row's
+// maximum grows by delta = max(0, rowmax(t) - C); then t, b and m move by -delta, +delta
+// and alpha = 2^(-delta/8) rescales A and l.  Rows that do not grow skip all of it: the
+// branch is taken per wave only when some row of the wave grew.
+//
+// Per tile and row, the rest of Eq. 6: r = sum of decoded codes; l += r; A += P R (FP8 MFMA).
+// The rank-one mean term r mu~_j^T also runs on the matrix unit: each row keeps the r of the
+// last 16 tiles (rho, rescaled with A when the maximum grows), and once per 16 tiles
+// A += mu~^T rho with the bf16 32x32x16 instruction (mu~ is exact bf16; rho is split into
+// bf16 hi + lo, 16 significant bits).  So the accumulator A is only touched by vector
+// instructions on the tiles where a row maximum grows.
 // Epilogue: O = bf16(A * sV / l) (App. B: one multiply by sV serves both terms).
 #include "vc_common.h"
 #include "vc_internal.h"
@@ -29,6 +42,7 @@
 namespace {
 
 constexpr int TILE_BYTES = 128 * 128;
+constexpr float EC_C = 119.65f;    // 120 + beta, beta = -0.35 (Eq. 7)
 
 // Byte offset of 16-byte chunk c16 (0..7) of row `row` in a 128 x 128-byte LDS tile; the
 // chunk index is XORed with row%8 so the 8 lanes served together hit 8 different bank groups.
@@ -43,10 +57,17 @@ __device__ __forceinline__ v8i lds_frag32(const uint8_t* tile, int row, int c16)
   return r;
 }
 
-__device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c) {
-  // cbsz = blgp = 0: both operands E4M3; E8M0 scales 127 = 2^0
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+// E4M3 x E4M3 -> float32, operands scaled by 2^(sa-127) and 2^(sb-127) (E8M0 block scales).
+__device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
+
+__device__ __forceinline__ v16f mfma_bf16(v8s a, v8s b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
+                                                 0, 0, 0);
+}
+
+constexpr int MRING = 32;   // LDS ring of mean rows: two 16-tile groups (one being summed, one filling)
 
 }  // namespace
 
@@ -60,7 +81,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
                                                   uint32_t G, float L, uint16_t* __restrict__ O) {
   __shared__ __attribute__((aligned(16))) uint8_t kt[2][TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t rt[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) float mus[2][128];
+  __shared__ __attribute__((aligned(16))) uint16_t mring[MRING][128];
   __shared__ float red[4];
 
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
@@ -70,20 +91,22 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
   const size_t headN = (size_t)bh * N;
   const int qi = qb * 128 + w * 32 + q;
 
-  // ---- prologue: Q block scale (amax over the 128 x 128 block) and E4M3 Q fragments ----
+  // ---- prologue: Q L, its block scale sQ = 2^E (amax over the 128 x 128 block), E4M3 ----
   const uint16_t* qrow = Q + (headN + qi) * VC_D;
-  uint4 qraw[2][4];
+  float qs[64];
   float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      qraw[c][m] = *(const uint4*)(qrow + 64 * c + 32 * g + 8 * m);
-      const uint32_t wd[4] = {qraw[c][m].x, qraw[c][m].y, qraw[c][m].z, qraw[c][m].w};
+      const uint4 raw = *(const uint4*)(qrow + 64 * c + 32 * g + 8 * m);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        amax = fmaxf(amax, fabsf(bf16_to_f32(wd[e] & 0xFFFFu)));
-        amax = fmaxf(amax, fabsf(bf16_to_f32(wd[e] >> 16)));
+        const float lo = bf16_to_f32(wd[e] & 0xFFFFu) * L, hi = bf16_to_f32(wd[e] >> 16) * L;
+        qs[32 * c + 8 * m + 2 * e] = lo;
+        qs[32 * c + 8 * m + 2 * e + 1] = hi;
+        amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
       }
     }
   amax = wave_max(amax);
@@ -99,29 +122,31 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       *(uint4*)(&kt[0][swz(row, c16)]) = ks[u];
       *(uint4*)(&rt[0][swz(row, c16)]) = rs[u];
     }
-    if (!NO_MEAN && t < 64) {
-      const uint32_t mr = *(const uint32_t*)(mu + (size_t)bh * T * VC_D + 2 * t);
-      mus[0][2 * t] = bf16_to_f32(mr & 0xFFFFu);
-      mus[0][2 * t + 1] = bf16_to_f32(mr >> 16);
+    if (!NO_MEAN) {
+      for (int i = t; i < MRING * 128 / 2; i += 256) ((uint32_t*)&mring[0][0])[i] = 0u;
+      __syncthreads();
+      if (t < 64) ((uint32_t*)&mring[0][0])[t] = *(const uint32_t*)(mu + (size_t)bh * T * VC_D + 2 * t);
     }
   }
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float sQ = amax == 0.0f ? 1.0f : amax / 448.0f;
+  const int EQ = pow2_block_exponent(amax);
+  const int sb = 127 + EQ;                         // E8M0 of sQ
+  const float qinv = __builtin_ldexpf(1.0f, -EQ);  // exact
   v8i qf[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t wd[4] = {qraw[c][m].x, qraw[c][m].y, qraw[c][m].z, qraw[c][m].w};
-      qf[c][2 * m] = (int)e4m3x4(bf16_to_f32(wd[0] & 0xFFFFu) / sQ, bf16_to_f32(wd[0] >> 16) / sQ,
-                                 bf16_to_f32(wd[1] & 0xFFFFu) / sQ, bf16_to_f32(wd[1] >> 16) / sQ);
-      qf[c][2 * m + 1] = (int)e4m3x4(bf16_to_f32(wd[2] & 0xFFFFu) / sQ, bf16_to_f32(wd[2] >> 16) / sQ,
-                                     bf16_to_f32(wd[3] & 0xFFFFu) / sQ, bf16_to_f32(wd[3] >> 16) / sQ);
+    for (int d4 = 0; d4 < 8; ++d4) {
+      const float* x = &qs[32 * c + 4 * d4];
+      qf[c][d4] = (int)e4m3x4(x[0] * qinv, x[1] * qinv, x[2] * qinv, x[3] * qinv);
     }
-  const float qa = L * sQ;
 
-  float m_run = -__builtin_inff(), l_run = 0.0f;
+  float b = 0.0f, l_run = 0.0f;   // b = 119.65 - m; set on the first tile
+  v16f bsplat = {};
+  float rho[8];                   // r of this group's tiles 8g .. 8g+7 (query q)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rho[k] = 0.0f;
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = v16f{};
@@ -144,29 +169,45 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       if (!NO_MEAN && t < 64) mr = *(const uint32_t*)(mu + ((size_t)bh * T + jn) * VC_D + 2 * t);
     }
 
-    // S^T = Kq_j . Qq^T
+    // t = a s + b from the matrix unit: S^T = Kq_j . Qq^T with block scales sK_j, sQ
+    const int sa = (int)((__float_as_uint(sK[(size_t)bh * T + j]) >> 23) & 0xFFu);  // E8M0 of sK_j
     v16f s[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = v16f{};
-#pragma unroll
-      for (int c = 0; c < 2; ++c) s[kb] = mfma_fp8(lds_frag32(kt[cur], 32 * kb + q, 4 * c + 2 * g), qf[c], s[kb]);
+      s[kb] = mfma_fp8(lds_frag32(kt[cur], 32 * kb + q, 2 * g), qf[0], bsplat, sa, sb);
+      s[kb] = mfma_fp8(lds_frag32(kt[cur], 32 * kb + q, 4 + 2 * g), qf[1], s[kb], sa, sb);
     }
 
-    // running maximum and the FMA constants of Eq. 7
-    const float a = qa * sK[(size_t)bh * T + j];
-    float mx = -__builtin_inff();
+    // running maximum (Eq. 1) in t's units
+    float tm = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float xhat = a * mx;
-    const float m_new = fmaxf(m_run, xhat);
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * 0.125f);
-    const float b = 119.65f - m_new;
+      for (int i = 0; i < 16; ++i) tm = fmaxf(tm, s[kb][i]);
+    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    const bool first = j == 0;
+    const float delta = first ? tm - EC_C : fmaxf(tm - EC_C, 0.0f);
+    if (first || __ballot(delta > 0.0f) != 0ull) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[kb][i] -= delta;
+      if (!first) {
+        const float alpha = __builtin_amdgcn_exp2f(-0.125f * delta);
+        l_run *= alpha;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rho[k] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+      }
+      b -= delta;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bsplat[i] = b;
+    }
 
-    // ExpCast: one FMA and one saturating RNE byte conversion per element.  Byte jj of the
+    // ExpCast Round + clip: one saturating RNE byte conversion per element.  Byte jj of the
     // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
     v8i pw[2];
 #pragma unroll
@@ -175,10 +216,10 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       for (int wd = 0; wd < 8; ++wd) {
         const int kb = 2 * p + (wd >> 2), i0 = 4 * (wd & 3);
         uint32_t word = 0;
-        word = expcast_byte(__builtin_fmaf(a, s[kb][i0 + 0], b), 0, word);
-        word = expcast_byte(__builtin_fmaf(a, s[kb][i0 + 1], b), 1, word);
-        word = expcast_byte(__builtin_fmaf(a, s[kb][i0 + 2], b), 2, word);
-        word = expcast_byte(__builtin_fmaf(a, s[kb][i0 + 3], b), 3, word);
+        word = expcast_byte(s[kb][i0 + 0], 0, word);
+        word = expcast_byte(s[kb][i0 + 1], 1, word);
+        word = expcast_byte(s[kb][i0 + 2], 2, word);
+        word = expcast_byte(s[kb][i0 + 3], 3, word);
         pw[p][wd] = (int)word;
       }
 
@@ -193,32 +234,40 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
         r += (lo[0] + lo[1]) + (hi[0] + hi[1]);
       }
     r += __shfl_xor(r, 32, 64);
-    l_run = alpha * l_run + r;
+    l_run += r;
 
-    // Eq. 6: rescale the numerator and add the rank-one mean term r mu~_j^T
+    // Eq. 6: the rank-one mean term r mu~_j^T, collected per 16-tile group (see the header)
+    if (!NO_MEAN) {
+      const int jl = j & 15;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int k = 0; k < 8; ++k) rho[k] = (g == (jl >> 3) && k == (jl & 7)) ? r : rho[k];
+      if (jl == 15 || j == T - 1) {
+        v8s bhi, blo;
 #pragma unroll
-      for (int ig = 0; ig < 4; ++ig) {
-        if (NO_MEAN) {
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t hi = f32_to_bf16_rne(rho[k]);
+          bhi[k] = (short)hi;
+          blo[k] = (short)f32_to_bf16_rne(rho[k] - bf16_to_f32(hi));
+          rho[k] = 0.0f;
+        }
+        const int t0 = (j & ~15) + 8 * g;   // first tile of this lane's K-slots
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[db][4 * ig + e] *= alpha;
-        } else {
-          const float4 m4 = *(const float4*)(&mus[cur][32 * db + 8 * ig + 4 * g]);
-          acc[db][4 * ig + 0] = __builtin_fmaf(r, m4.x, acc[db][4 * ig + 0] * alpha);
-          acc[db][4 * ig + 1] = __builtin_fmaf(r, m4.y, acc[db][4 * ig + 1] * alpha);
-          acc[db][4 * ig + 2] = __builtin_fmaf(r, m4.z, acc[db][4 * ig + 2] * alpha);
-          acc[db][4 * ig + 3] = __builtin_fmaf(r, m4.w, acc[db][4 * ig + 3] * alpha);
+        for (int db = 0; db < 4; ++db) {
+          v8s am;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) am[k] = (short)mring[(t0 + k) % MRING][32 * db + q];
+          acc[db] = mfma_bf16(am, bhi, acc[db]);
+          acc[db] = mfma_bf16(am, blo, acc[db]);
         }
       }
+    }
 
     // O^T += Rq_j^T . P^T
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int p = 0; p < 2; ++p) acc[db] = mfma_fp8(lds_frag32(rt[cur], 32 * db + q, 4 * p + 2 * g), pw[p], acc[db]);
-
-    m_run = m_new;
+      for (int p = 0; p < 2; ++p)
+        acc[db] = mfma_fp8(lds_frag32(rt[cur], 32 * db + q, 4 * p + 2 * g), pw[p], acc[db], 127, 127);
 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -226,10 +275,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       *(uint4*)(&kt[cur ^ 1][swz(row, c16)]) = kr[i];
       *(uint4*)(&rt[cur ^ 1][swz(row, c16)]) = rr[i];
     }
-    if (!NO_MEAN && t < 64) {
-      mus[cur ^ 1][2 * t] = bf16_to_f32(mr & 0xFFFFu);
-      mus[cur ^ 1][2 * t + 1] = bf16_to_f32(mr >> 16);
-    }
+    if (!NO_MEAN && t < 64) ((uint32_t*)&mring[jn % MRING][0])[t] = mr;
     __syncthreads();
   }
 

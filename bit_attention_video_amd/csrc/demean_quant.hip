@@ -9,7 +9,8 @@
 // Passes (all grids are (blocks, b*h); 256 threads = 32 channel quads x 8 row groups):
 //   k_kstat_partial  float64 channel sums of K per 1024-row chunk
 //   k_kstat_final    kbar = float32(sum / N) in chunk order
-//   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = amax/448, codes
+//   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = 2^E (smallest power of two
+//                    with amax <= 448 sK, an E8M0 block scale), codes
 //   k_vclear         zero the per-channel |R| maxima
 //   k_vpass1         per block of V[pi]: mu_j (float64 sum / 128), |R| maxima -> atomicMax
 //   k_vpass2         sV = amax/448; codes of R / sV into the tile-transposed PV operand order;
@@ -94,11 +95,13 @@ __global__ __launch_bounds__(256) void k_kquant(const uint16_t* __restrict__ K, 
     for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
   }
   amax = block_max_256(amax, red4);
-  const float s = amax == 0.0f ? 1.0f : amax / 448.0f;
+  const int E = pow2_block_exponent(amax);
+  const float inv = __builtin_ldexpf(1.0f, -E);   // exact: the scale is a power of two
+  const float s = __builtin_ldexpf(1.0f, E);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = j * VC_BLK + rg + 8 * i;
-    const uint32_t w = e4m3x4(x[i][0] / s, x[i][1] / s, x[i][2] / s, x[i][3] / s);
+    const uint32_t w = e4m3x4(x[i][0] * inv, x[i][1] * inv, x[i][2] * inv, x[i][3] * inv);
     *(uint32_t*)(Kq + ((size_t)bh * N + r) * VC_D + 4 * q4) = w;
   }
   if (t == 0) sK[(size_t)bh * (N / VC_BLK) + j] = s;

@@ -53,6 +53,19 @@ __device__ __forceinline__ uint32_t expcast_byte(float t, uint32_t sel, uint32_t
   return __builtin_amdgcn_cvt_pk_u8_f32(t, sel, old);
 }
 
+// Exponent E of the smallest power of two 2^E with amax <= 448 * 2^E (0 when amax == 0,
+// never below -100 so 2^E and 2^-E stay normal floats): with amax = m 2^e, m in [0.5, 1),
+// 448 * 2^(e-8) always fits and 448 * 2^(e-10) never does.  The Q/K block scales are these
+// powers of two, i.e. E8M0 values the FP8 matrix instructions apply themselves.
+__device__ __forceinline__ int pow2_block_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e;
+  (void)__builtin_frexpf(amax, &e);
+  int E = e - 8;
+  if (amax <= __builtin_ldexpf(448.0f, E - 1)) E -= 1;
+  return E < -100 ? -100 : E;
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

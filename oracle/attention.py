@@ -15,10 +15,12 @@ VC-Attention (arXiv 2609.15810):
 
 The emulated path follows those steps in that order, tile by tile (tiles of 128
 keys, j increasing), on the same quantised operands the kernel receives.  Its
-float32 steps are the ones that decide a code; everything else is float64:
+float32 steps are the ones that decide a code; everything else is float64.
+The query operand already carries L = fl32(8 log2(e) softmax_scale) (it is
+quantised as fl32(Q L), see vsmooth.quantize_q), so with power-of-two block
+scales the slope of Eq. 7 is exact:
 
-  qa   = fl32(L * s_Q)            L = fl32(8 log2(e) * softmax_scale)
-  a    = fl32(qa * s_K[j])        one scale per (query block, key tile)
+  a    = s_Q * s_K[j]             one scale per (query block, key tile)
   s    = fl32(Q-hat . K-hat)      the FP32 score of two E4M3 operands
   xhat = fl32(a * rowmax_j s)     running maximum, in units of 8 log2(e) S
   m'   = max(m, xhat);  b = fl32(C - m'),  C = fl32(120 + beta)
@@ -74,10 +76,11 @@ def _log2e_scale(scale: float) -> np.float32:
 
 def attention_tiled(Qv, sQ, Kv, sK, Rv, mu_t, sV, scale: Optional[float] = None,
                     p_mode: str = "expcast", rows: Optional[Sequence[int]] = None,
-                    round_output: bool = True):
+                    round_output: bool = True, q_prescaled: bool = True):
     """Emulated tiled VC attention for one (batch, head).
 
-    Qv   (N, d)      query operand values (decoded E4M3 codes, or real values)
+    Qv   (N, d)      query operand values (decoded E4M3 codes of fl32(Q L) / s_Q when
+                     q_prescaled, else raw query values that still need L)
     sQ   (N/128,)    query block scales
     Kv   (N, d)      key operand values in permuted order
     sK   (N/128,)    key tile scales
@@ -99,8 +102,12 @@ def attention_tiled(Qv, sQ, Kv, sK, Rv, mu_t, sV, scale: Optional[float] = None,
     nq = len(rows)
     L = _log2e_scale(scale)
     sQr = np.asarray(sQ)[rows // BQ]
-    qa = fl32(np.float32(L) * fl32(sQr))                                   # (nq,) float32
-    qa64 = 8.0 * np.log2(np.e) * scale * np.asarray(sQr, dtype=np.float64)  # exact mode only
+    if q_prescaled:
+        qa = fl32(sQr)                                                     # L is inside Q-hat
+        qa64 = qa.astype(np.float64)                                       # exact: powers of two
+    else:
+        qa = fl32(np.float32(L) * fl32(sQr))                               # (nq,) float32
+        qa64 = 8.0 * np.log2(np.e) * scale * np.asarray(sQr, dtype=np.float64)  # exact mode only
     Qr = Qv[rows]
     m = np.full(nq, -np.inf)
     l = np.zeros(nq)
@@ -150,7 +157,7 @@ def vc_attention_emulated(Q, K, V, perm, scale=None, p_mode="expcast", rows=None
     from . import vsmooth
     N = Q.shape[0]
     perm = np.arange(N) if perm is None else np.asarray(perm)
-    qc, sQ = vsmooth.quantize_q(Q)
+    qc, sQ = vsmooth.quantize_q(Q, scale)
     if k_smooth:
         kc, sK = vsmooth.quantize_k(K, perm)
     else:

@@ -22,12 +22,16 @@ Readings taken where the pages are silent (all documented in the design notes):
     Labels are those of the last assignment; the objective J uses those labels
     and the means recomputed from them.
   * pi is the stable argsort (ties keep token order).
-  * K and Q scales: one per 128-row block, amax/448; V scale: one per
-    (batch, head, channel) over all N tokens, amax|R|/448; a zero amax gives
+  * K and Q scales: one per 128-row block, the smallest power of two 2^E with
+    amax <= 448 * 2^E (an E8M0 block scale); the Q block is quantised after
+    multiplying by L = fl32(8 log2(e) softmax_scale), so Q-hat . K-hat times
+    s_Q s_K is the score in the units of Eq. 7's FMA.  V scale: one per
+    (batch, head, channel) over all N tokens, amax|R|/448.  A zero amax gives
     scale 1.  Means are float32 (an exact sum rounded once), stored for the
     kernel as bf16(mu / s_V).
   * Quantisation decisions are taken in float32: x/s is one correctly rounded
-    float32 division, then E4M3 round-to-nearest-even.
+    float32 division (exact for the power-of-two scales), then E4M3
+    round-to-nearest-even.
 """
 from __future__ import annotations
 
@@ -120,12 +124,28 @@ def _scale_from_amax(amax) -> np.ndarray:
     return np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
 
 
+def pow2_scale(amax) -> np.ndarray:
+    """Smallest power of two 2^E with amax <= 448 * 2^E (1 where amax == 0), as float32.
+
+    With amax = m 2^e (m in [0.5, 1)): 448 * 2^(e-8) = 1.75 * 2^e always fits, 448 * 2^(e-10)
+    never does, so E is e - 9 when amax <= 448 * 2^(e-9) and e - 8 otherwise.  E is kept at
+    or above -100 so the scale and its inverse are normal floats (blocks that small are
+    all-but-zero; their codes underflow either way).
+    """
+    amax = np.asarray(amax, dtype=np.float64)
+    _, e = np.frexp(amax)
+    E = e.astype(np.int64) - 8
+    E = np.where(amax <= np.ldexp(E4M3_MAX, E - 1), E - 1, E)
+    E = np.maximum(E, -100)
+    return np.where(amax > 0, np.ldexp(1.0, E), 1.0).astype(np.float32)
+
+
 def quantize_rows_per_block(X32: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """Per 128-row block of a float32 (N, d) array: s_b = amax/448, codes = E4M3(fl32(x / s_b))."""
+    """Per 128-row block of a float32 (N, d) array: s_b = pow2_scale(amax), codes = E4M3(x / s_b)."""
     N, d = X32.shape
     blocks = X32.reshape(N // BV, BV, d)
-    s = _scale_from_amax(np.abs(blocks).max(axis=(1, 2)))
-    codes = e4m3_encode(blocks / s[:, None, None])         # float32 division, then E4M3 RNE
+    s = pow2_scale(np.abs(blocks).max(axis=(1, 2)))
+    codes = e4m3_encode(blocks / s[:, None, None])         # exact float32 scaling, then E4M3 RNE
     return codes.reshape(N, d), s
 
 
@@ -146,9 +166,18 @@ def quantize_k(K, perm) -> Tuple[np.ndarray, np.ndarray]:
     return quantize_rows_per_block(Ks)
 
 
-def quantize_q(Q) -> Tuple[np.ndarray, np.ndarray]:
-    """Q path: per 128-row block E4M3 (Q keeps its token order, Eq. 3)."""
-    return quantize_rows_per_block(fl32(Q))
+def log2e_scale(softmax_scale: float, d: int = 128) -> np.float32:
+    """L = fl32(8 log2(e) softmax_scale): Eq. 7's slope a = 8 log2(e) times the softmax scale."""
+    if softmax_scale is None:
+        softmax_scale = 1.0 / np.sqrt(d)
+    return np.float32(8.0 * np.log2(np.e) * softmax_scale)
+
+
+def quantize_q(Q, softmax_scale=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Q path: fl32(Q * L), then per 128-row block E4M3 (Q keeps its token order, Eq. 3)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    L = log2e_scale(softmax_scale, Q.shape[1])
+    return quantize_rows_per_block((fl32(Q) * L).astype(np.float32))
 
 
 def block_means(Vp) -> np.ndarray:

@@ -17,8 +17,8 @@ pytestmark = pytest.mark.gpu
 TOL = 5e-3   # acceptance: rel-L2 of the GPU output against the emulated oracle, same permutation
 
 
-def _oracle_ops(Qh, Kh, Vh, perm, demean=True):
-    qc, sQ = S.quantize_q(Qh)
+def _oracle_ops(Qh, Kh, Vh, perm, demean=True, scale=None):
+    qc, sQ = S.quantize_q(Qh, scale)
     kc, sK = S.quantize_k(Kh, perm)
     vq = S.quantize_v(Vh, perm, demean=demean)
     return {"qc": qc, "sQ": sQ, "kc": kc, "sK": sK, **vq}
@@ -125,7 +125,7 @@ def test_attn_fwd_small_and_ragged_shapes():
         for b in range(B):
             for h in range(H):
                 Qh, Kh, Vh = values(Q[b, h]), values(K[b, h]), values(V[b, h])
-                ops = _oracle_ops(Qh, Kh, Vh, perm[b, h])
+                ops = _oracle_ops(Qh, Kh, Vh, perm[b, h], scale=0.05)
                 ref = T.attention_tiled(F.e4m3_decode(ops["qc"]), ops["sQ"], F.e4m3_decode(ops["kc"]), ops["sK"],
                                         F.e4m3_decode(ops["codes"]), ops["mu_t"], ops["sV"], scale=0.05)
                 assert T.rel_l2(O[b, h], ref) < TOL

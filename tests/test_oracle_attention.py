@@ -66,15 +66,18 @@ def test_tiled_recurrence_exact_mode_equals_exact_attention(demean):
         mu = np.zeros((N // 128, d))
         R = Vp
     ones = np.ones(N // 128)
-    O = T.attention_tiled(Q, ones, Kp, ones, R, mu, np.ones(d), p_mode="exact", round_output=False)
+    O = T.attention_tiled(Q, ones, Kp, ones, R, mu, np.ones(d), p_mode="exact", round_output=False,
+                          q_prescaled=False)
     assert np.allclose(O, T.attention_exact(Q, K, V), rtol=0, atol=1e-11)
     # scaling R and mu by 1/sV and multiplying back in the epilogue (App. B) changes nothing
     sV = np.exp(np.random.default_rng(7).uniform(-2, 2, d))
-    O2 = T.attention_tiled(Q, ones, Kp, ones, R / sV, mu / sV, sV, p_mode="exact", round_output=False)
+    O2 = T.attention_tiled(Q, ones, Kp, ones, R / sV, mu / sV, sV, p_mode="exact", round_output=False,
+                           q_prescaled=False)
     assert np.allclose(O2, O, atol=1e-11)
     # a row subset gives the same rows
     rows = np.array([0, 127, 128, 511])
-    O3 = T.attention_tiled(Q, ones, Kp, ones, R, mu, np.ones(d), p_mode="exact", rows=rows, round_output=False)
+    O3 = T.attention_tiled(Q, ones, Kp, ones, R, mu, np.ones(d), p_mode="exact", rows=rows, round_output=False,
+                           q_prescaled=False)
     assert np.allclose(O3, O[rows], atol=1e-13)
 
 
@@ -90,7 +93,7 @@ def test_tiled_expcast_rows_obey_prop31(golden):
         V = rng.standard_normal((N, d)) * 2 + rng.standard_normal(d)
         ones = np.ones(N // 128)
         O = T.attention_tiled(Q, ones, K, ones, V, np.zeros((N // 128, d)), np.ones(d),
-                              p_mode="expcast", round_output=False)
+                              p_mode="expcast", round_output=False, q_prescaled=False)
         Oe = T.attention_exact(Q, K, V)
         S_ = (Q @ K.T) / np.sqrt(d)
         u = (S_ - S_.max(1, keepdims=True)) * np.log2(np.e)
@@ -136,3 +139,14 @@ def test_vsmooth_beats_unsmoothed_baseline_on_grouped_values():
     O_vc, _ = T.vc_attention_emulated(Q, K, V, grp["perm"])
     O_base, _ = T.vc_attention_emulated(Q, K, V, None, demean=False)
     assert T.rel_l2(O_vc, Oe) < T.rel_l2(O_base, Oe)
+
+
+def test_prescaled_query_operand_equals_raw_query_path():
+    # Folding the slope 8 log2(e) / sqrt(d) into the query operand (what vsmooth.quantize_q does
+    # before quantising) gives the same attention as applying it in the recurrence.
+    Q, K, V = _qkv(12, N=256)
+    ones = np.ones(2)
+    Qs = Q * (8 * np.log2(np.e) / np.sqrt(128))
+    O = T.attention_tiled(Qs, ones, K, ones, V, np.zeros((2, 128)), np.ones(128), p_mode="exact",
+                          round_output=False, q_prescaled=True)
+    assert np.allclose(O, T.attention_exact(Q, K, V), atol=1e-11)

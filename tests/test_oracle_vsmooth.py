@@ -106,10 +106,11 @@ def test_permuted_quantisers_blocks():
     codes, sK = S.quantize_k(K, perm)
     Kp = F.fl32(K[perm]) - S.key_channel_mean(K)[None, :]
     deq = F.e4m3_decode(codes) * np.repeat(sK, 128)[:, None]
-    # each block's largest entry maps to the largest code; every element within half an E4M3 step
+    # each block's largest entry lands in the top binade of E4M3 (power-of-two scale), every
+    # element within half an E4M3 step
     for b in range(N // 128):
         blk = np.abs(F.e4m3_decode(codes[b * 128:(b + 1) * 128]))
-        assert blk.max() == 448.0
+        assert 224.0 <= blk.max() <= 448.0
     err = np.abs(deq - Kp)
     assert np.all(err <= np.abs(Kp) * 2.0 ** -4 + np.repeat(sK, 128)[:, None] * 2.0 ** -10 + 1e-12)
     # channel mean of the smoothed keys is ~0
@@ -149,3 +150,30 @@ def test_sorting_lowers_value_error_on_grouped_values():
         return np.sqrt(((rec.reshape(N, d) - V[perm]) ** 2).mean())
     grp = S.vsmooth_group(V, k=G, iters=10)
     assert rmse(grp["perm"]) < 0.7 * rmse(np.arange(N))
+
+
+def test_pow2_block_scale_definition():
+    rng = np.random.default_rng(10)
+    amax = np.concatenate([rng.uniform(0, 1e4, 10000), np.ldexp(448.0, np.arange(-20, 20)),
+                           np.nextafter(np.ldexp(448.0, np.arange(-20, 20)), np.inf), [0.0, 1e-30]])
+    s = S.pow2_scale(amax).astype(np.float64)
+    m, e = np.frexp(s)
+    assert np.all(m == 0.5)                                       # powers of two
+    pos = amax > 0
+    assert np.all(amax[pos] <= 448.0 * s[pos])                   # the block fits E4M3
+    big = amax > 448.0 * 2.0 ** -101
+    assert np.all(amax[big] > 224.0 * s[big])                    # and the scale is the smallest such
+    assert np.all(s[pos & ~big] == 2.0 ** -100)                  # floor for all-but-zero blocks
+    assert np.all(s[~pos] == 1.0)
+
+
+def test_q_quantiser_folds_log2e_scale():
+    rng = np.random.default_rng(11)
+    Q = F.bf16_round(rng.standard_normal((256, 128)))
+    codes, sQ = S.quantize_q(Q)
+    L = np.float32(8.0 * np.log2(np.e) / np.sqrt(128))
+    deq = F.e4m3_decode(codes) * np.repeat(sQ, 128)[:, None]
+    Qs = F.fl32(Q) * L
+    assert np.all(np.abs(deq - Qs) <= np.abs(Qs) * 2.0 ** -4 + np.repeat(sQ, 128)[:, None] * 2.0 ** -10)
+    codes2, sQ2 = S.quantize_q(Q, softmax_scale=0.5)
+    assert not np.array_equal(sQ2, sQ) or not np.array_equal(codes2, codes)
