@@ -27,6 +27,17 @@ sys.path.insert(0, ROOT)
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, vendor figure
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "attn_fwd_video_traffic.json")
+ATTN_SOURCES = ["bit_attention_video_amd/csrc/attn_fwd.hip", "bit_attention_video_amd/csrc/vc_common.h"]
+
+
+def attn_source_hash():
+    """Hash of the attention kernel's sources: counters taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def log(msg):
@@ -149,7 +160,7 @@ def main():
     if os.path.exists(PROFILE_TRAFFIC):
         with open(PROFILE_TRAFFIC) as f:
             tr = json.load(f)
-        if tr.get("config") == cfg.name:
+        if tr.get("config") == cfg.name and tr.get("kernel_source_sha256_16") == attn_source_hash():
             traffic = tr.get("bytes_per_launch")
     # V-Smooth cost relative to attention (the pages' schedule: 40 steps, grouping at steps 0, 4, 8,
     # demeaning on the first 25% of steps; the reuse window: group once, demean each of 4 steps)
