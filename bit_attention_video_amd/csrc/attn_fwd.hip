@@ -3,7 +3,8 @@
 //
 // One workgroup = 4 waves = one 128-row query block of one (b, h); wave w owns queries
 // 32w .. 32w+31.  Keys/values stream in tiles of 128 (= B_v, so each tile has one key
-// scale sK_j and one mean mu_j), double-buffered through LDS.
+// scale sK_j and one mean mu_j), double-buffered in LDS and filled by direct global->LDS
+// loads (no staging registers).
 //
 // Layouts.  Both products use the FP8 32x32x64 matrix instruction with the key index as the
 // reduction dimension of PV, computed transposed so one lane owns one query row:
@@ -44,9 +45,36 @@ namespace {
 constexpr int TILE_BYTES = 128 * 128;
 constexpr float EC_C = 119.65f;    // 120 + beta, beta = -0.35 (Eq. 7)
 
-// Byte offset of 16-byte chunk c16 (0..7) of row `row` in a 128 x 128-byte LDS tile; the
-// chunk index is XORed with row%8 so the 8 lanes served together hit 8 different bank groups.
-__device__ __forceinline__ int swz(int row, int c16) { return row * 128 + ((c16 ^ (row & 7)) << 4); }
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Byte offset of 16-byte chunk c16 (0..7) of row `row` in a 128 x 128-byte LDS tile.  The
+// chunk index is XORed with (row % 8) ^ (row / 8 % 2): rows r..r+7 then hit 8 different
+// 16-byte bank groups of a 128-byte bank period, and rows r..r+15 hit 16 different groups
+// of a 256-byte period, so the lanes one LDS cycle serves never share a bank.
+__device__ __forceinline__ int swz_phys(int row, int c16) { return c16 ^ (row & 7) ^ ((row >> 3) & 1); }
+__device__ __forceinline__ int swz(int row, int c16) { return row * 128 + (swz_phys(row, c16) << 4); }
+
+// Values of lanes q and q+32 (v_permlane32_swap returns both in every lane).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Direct global -> LDS copy of one 16 KB tile into the swizzled layout: wave w, instruction i
+// fills LDS chunks (4w + i) * 64 + lane, so each lane fetches the global chunk that belongs there.
+__device__ __forceinline__ void stage_tile(const uint8_t* gtile, uint8_t* ltile, int w, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int P = (4 * w + i) * 64 + lane;
+    const int row = P >> 3, c16 = swz_phys(row, P & 7);   // the XOR is an involution
+    __builtin_amdgcn_global_load_lds((const void*)(gtile + row * 128 + c16 * 16),
+                                     (lds_void*)(ltile + (4 * w + i) * 1024), 16, 0, 0);
+  }
+}
 
 __device__ __forceinline__ v8i lds_frag32(const uint8_t* tile, int row, int c16) {
   const uint4 lo = *(const uint4*)(tile + swz(row, c16));
@@ -67,6 +95,9 @@ __device__ __forceinline__ v16f mfma_bf16(v8s a, v8s b, v16f c) {
                                                  0, 0, 0);
 }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+constexpr v2bf BF16_ONES = {(__bf16)1.0f, (__bf16)1.0f};
+
 constexpr int MRING = 32;   // LDS ring of mean rows: two 16-tile groups (one being summed, one filling)
 
 }  // namespace
@@ -79,9 +110,9 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
                                                   const uint16_t* __restrict__ mu,
                                                   const float* __restrict__ sV, int N, int nqb,
                                                   uint32_t G, float L, uint16_t* __restrict__ O) {
-  __shared__ __attribute__((aligned(16))) uint8_t kt[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t rt[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) uint16_t mring[MRING][128];
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t rt[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) uint16_t mring[MRING][128];
   __shared__ float red[4];
 
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
@@ -90,6 +121,15 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
   const int T = N / 128;
   const size_t headN = (size_t)bh * N;
   const int qi = qb * 128 + w * 32 + q;
+  const uint8_t* Kh = Kq + headN * VC_D;
+  const uint8_t* Rh = Rq + (size_t)bh * T * TILE_BYTES;
+  const uint16_t* muh = mu + (size_t)bh * T * VC_D;
+
+  // stage tile 0 (and clear the mean ring)
+  stage_tile(Kh, kt[0], w, lane);
+  stage_tile(Rh, rt[0], w, lane);
+  if (!NO_MEAN)
+    for (int i = t; i < MRING * 128 / 2; i += 256) ((uint32_t*)&mring[0][0])[i] = 0u;
 
   // ---- prologue: Q L, its block scale sQ = 2^E (amax over the 128 x 128 block), E4M3 ----
   const uint16_t* qrow = Q + (headN + qi) * VC_D;
@@ -112,23 +152,9 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
   amax = wave_max(amax);
   if (lane == 0) red[w] = amax;
 
-  // stage tile 0
-  {
-    const uint4* ks = (const uint4*)(Kq + headN * VC_D);
-    const uint4* rs = (const uint4*)(Rq + (size_t)bh * T * TILE_BYTES);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = t + 256 * i, row = u >> 3, c16 = u & 7;
-      *(uint4*)(&kt[0][swz(row, c16)]) = ks[u];
-      *(uint4*)(&rt[0][swz(row, c16)]) = rs[u];
-    }
-    if (!NO_MEAN) {
-      for (int i = t; i < MRING * 128 / 2; i += 256) ((uint32_t*)&mring[0][0])[i] = 0u;
-      __syncthreads();
-      if (t < 64) ((uint32_t*)&mring[0][0])[t] = *(const uint32_t*)(mu + (size_t)bh * T * VC_D + 2 * t);
-    }
-  }
-  __syncthreads();
+  __syncthreads();   // red[] and the cleared ring
+  if (!NO_MEAN && w == 0)
+    __builtin_amdgcn_global_load_lds((const void*)(muh + 2 * lane), (lds_void*)&mring[0][0], 4, 0, 0);
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int EQ = pow2_block_exponent(amax);
   const int sb = 127 + EQ;                         // E8M0 of sQ
@@ -141,6 +167,8 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       const float* x = &qs[32 * c + 4 * d4];
       qf[c][d4] = (int)e4m3x4(x[0] * qinv, x[1] * qinv, x[2] * qinv, x[3] * qinv);
     }
+  __builtin_amdgcn_s_waitcnt(0);   // tile 0 and its mean row have landed in LDS
+  __syncthreads();
 
   float b = 0.0f, l_run = 0.0f;   // b = 119.65 - m; set on the first tile
   v16f bsplat = {};
@@ -153,20 +181,12 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
 
   for (int j = 0; j < T; ++j) {
     const int cur = j & 1;
-    // prefetch tile j+1 into registers (the last iteration re-reads tile T-1 into the idle
-    // buffer, which keeps the loop free of branches around the loads)
-    const int jn = j + 1 < T ? j + 1 : j;
-    uint4 kr[4], rr[4];
-    uint32_t mr = 0;
-    {
-      const uint4* ks = (const uint4*)(Kq + (headN + (size_t)jn * 128) * VC_D);
-      const uint4* rs = (const uint4*)(Rq + ((size_t)bh * T + jn) * TILE_BYTES);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kr[i] = ks[t + 256 * i];
-        rr[i] = rs[t + 256 * i];
-      }
-      if (!NO_MEAN && t < 64) mr = *(const uint32_t*)(mu + ((size_t)bh * T + jn) * VC_D + 2 * t);
+    if (j + 1 < T) {   // prefetch tile j+1 into the idle buffer (freed by the last barrier)
+      stage_tile(Kh + (size_t)(j + 1) * TILE_BYTES, kt[cur ^ 1], w, lane);
+      stage_tile(Rh + (size_t)(j + 1) * TILE_BYTES, rt[cur ^ 1], w, lane);
+      if (!NO_MEAN && w == 0)
+        __builtin_amdgcn_global_load_lds((const void*)(muh + (size_t)(j + 1) * VC_D + 2 * lane),
+                                         (lds_void*)&mring[(j + 1) % MRING][0], 4, 0, 0);
     }
 
     // t = a s + b from the matrix unit: S^T = Kq_j . Qq^T with block scales sK_j, sQ
@@ -184,7 +204,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) tm = fmaxf(tm, s[kb][i]);
-    tm = fmaxf(tm, __shfl_xor(tm, 32, 64));
+    tm = pair_max(tm);
     const bool first = j == 0;
     const float delta = first ? tm - EC_C : fmaxf(tm - EC_C, 0.0f);
     if (first || __ballot(delta > 0.0f) != 0ull) {
@@ -207,11 +227,13 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       for (int i = 0; i < 16; ++i) bsplat[i] = b;
     }
 
-    // ExpCast Round + clip: one saturating RNE byte conversion per element.  Byte jj of the
-    // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
+    // ExpCast Round + clip: one saturating RNE byte conversion per element, then the PV
+    // product of that key half.  Byte jj of the PV B-operand for key half p is element
+    // (kb = 2p + jj/16, i = jj%16) of S^T.
     v8i pw[2];
+    float r = 0.0f;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
         const int kb = 2 * p + (wd >> 2), i0 = 4 * (wd & 3);
@@ -222,18 +244,21 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
         word = expcast_byte(s[kb][i0 + 3], 3, word);
         pw[p][wd] = (int)word;
       }
-
-    // row sum of the decoded codes (the values the PV instruction consumes)
-    float r = 0.0f;
+      // O^T += Rq_j^T . P^T for this key half
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+      for (int db = 0; db < 4; ++db)
+        acc[db] = mfma_fp8(lds_frag32(rt[cur], 32 * db + q, 4 * p + 2 * g), pw[p], acc[db], 127, 127);
+      // row sum of the decoded codes (the values the PV instruction consumes): E4M3 values
+      // are exact in bf16, and a bf16 dot with (1, 1) adds a pair into the float32 sum
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
-        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(pw[p][wd], false);
-        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(pw[p][wd], true);
-        r += (lo[0] + lo[1]) + (hi[0] + hi[1]);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pw[p][wd], 1.0f, false),
+                                            BF16_ONES, r, false);
+        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pw[p][wd], 1.0f, true),
+                                            BF16_ONES, r, false);
       }
-    r += __shfl_xor(r, 32, 64);
+    }
+    r = pair_sum(r);
     l_run += r;
 
     // Eq. 6: the rank-one mean term r mu~_j^T, collected per 16-tile group (see the header)
@@ -262,20 +287,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       }
     }
 
-    // O^T += Rq_j^T . P^T
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        acc[db] = mfma_fp8(lds_frag32(rt[cur], 32 * db + q, 4 * p + 2 * g), pw[p], acc[db], 127, 127);
-
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int u = t + 256 * i, row = u >> 3, c16 = u & 7;
-      *(uint4*)(&kt[cur ^ 1][swz(row, c16)]) = kr[i];
-      *(uint4*)(&rt[cur ^ 1][swz(row, c16)]) = rr[i];
-    }
-    if (!NO_MEAN && t < 64) ((uint32_t*)&mring[jn % MRING][0])[t] = mr;
+    __builtin_amdgcn_s_waitcnt(0);   // the prefetched tile has landed before the barrier publishes it
     __syncthreads();
   }
 
