@@ -1,17 +1,24 @@
 // FP8 VC-Attention forward on gfx950 (VC-Attention Sec. 3.1 Eq. 1, Sec. 3.2 Eq. 6,
 // Sec. 3.3 Eq. 7, App. B).
 //
-// One workgroup = 4 waves = one 128-row query block of one (b, h); wave w owns queries
-// 32w .. 32w+31.  Keys/values stream in tiles of 128 (= B_v, so each tile has one key
-// scale sK_j and one mean mu_j), double-buffered in LDS and filled by direct global->LDS
-// loads (no staging registers).
+// One workgroup = 8 waves in two groups of four; group g owns the 128-row query block
+// 2 wb + g of one (b, h) and each of its waves owns 32 of those queries.  Keys/values stream
+// in tiles of 128 (= B_v, so each tile has one key scale sK_j and one mean mu_j) through
+// LDS, filled by direct global->LDS copies that every wave shares.
+//
+// Ping-pong between the two groups.  Per tile a wave has a matrix part M(j) -- the QK
+// product of tile j, the PV product and the row sum of tile j-1 -- and a vector part V(j):
+// the running maximum and the ExpCast codes of tile j.  The groups run them in opposite
+// phases separated by workgroup barriers (group 0: M(j) | V(j), group 1: V(j-1) | M(j)).  A
+// SIMD holds one wave of each group, so while one of them keeps the matrix unit busy the
+// other does the vector work; with one workgroup per CU nothing else competes.
 //
 // Layouts.  Both products use the FP8 32x32x64 matrix instruction with the key index as the
 // reduction dimension of PV, computed transposed so one lane owns one query row:
 //   S^T (keys x queries) = Kq_j (keys x d) . Qq^T (d x queries)
 //   O^T (d x queries)   += Rq_j^T (d x keys) . P^T (keys x queries)
-// In the 32x32 result layout lane (q = lane%32, g = lane/32) holds column q and rows
-// 8(i/4) + 4g + i%4 (i = 0..15), so every score, row statistic and output element of a
+// In the 32x32 result layout lane (q = lane%32, h = lane/32) holds column q and rows
+// 8(i/4) + 4h + i%4 (i = 0..15), so every score, row statistic and output element of a
 // lane belongs to query q; the lanes q and q+32 share a row and exchange one value.
 // The P bytes a lane produces are exactly its B-operand bytes for PV once the residual
 // tile is stored in the matching key order (vc_vsmooth_demean_quant's tile-transposed Rq).
@@ -29,23 +36,26 @@
 // and alpha = 2^(-delta/8) rescales A and l.  Rows that do not grow skip all of it: the
 // branch is taken per wave only when some row of the wave grew.
 //
-// Per tile and row, the rest of Eq. 6: r = sum of decoded codes; l += r; A += P R (FP8 MFMA).
-// The rank-one mean term r mu~_j^T also runs on the matrix unit: each row keeps the r of the
-// last 16 tiles (rho, rescaled with A when the maximum grows), and once per 16 tiles
-// A += mu~^T rho with the bf16 32x32x16 instruction (mu~ is exact bf16; rho is split into
-// bf16 hi + lo, 16 significant bits).  So the accumulator A is only touched by vector
-// instructions on the tiles where a row maximum grows.
+// Row sum (Eq. 6, r = sum of the decoded codes) on the matrix unit as well: a 16x16x128 FP8
+// product of a constant 0/1 operand with the P bytes returns each lane the sum of its
+// query's 128 codes (see rowsum_ones).  l += r.  The rank-one mean term r mu~_j^T runs on
+// the matrix unit too: each row keeps the r of the last 16 tiles (rho, rescaled with A when
+// the maximum grows), and once per 16 tiles A += mu~^T rho with the bf16 32x32x16
+// instruction (mu~ is exact bf16; rho is split into bf16 hi + lo, 16 significant bits).
 // Epilogue: O = bf16(A * sV / l) (App. B: one multiply by sV serves both terms).
 #include "vc_common.h"
 #include "vc_internal.h"
 #include "vc_attn.h"
 
+#include <type_traits>
+
 namespace {
 
 constexpr int TILE_BYTES = 128 * 128;
 constexpr float EC_C = 119.65f;    // 120 + beta, beta = -0.35 (Eq. 7)
-
-typedef __attribute__((address_space(3))) void lds_void;
+constexpr int NWAVE = 8;           // two groups of four waves
+constexpr int MRING = 32;          // LDS ring of mean rows: two 16-tile groups
+constexpr int NBUF = 2;            // K and R tile buffers each (prefetch depth NBUF - 1 tiles)
 
 // Byte offset of 16-byte chunk c16 (0..7) of row `row` in a 128 x 128-byte LDS tile.  The
 // chunk index is XORed with (row % 8) ^ (row / 8 % 2): rows r..r+7 then hit 8 different
@@ -54,26 +64,51 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ int swz_phys(int row, int c16) { return c16 ^ (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int c16) { return row * 128 + (swz_phys(row, c16) << 4); }
 
-// Values of lanes q and q+32 (v_permlane32_swap returns both in every lane).
+// Maximum of lanes q and q+32 (v_permlane32_swap returns both in every lane).
 __device__ __forceinline__ float pair_max(float x) {
   const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+
+// Direct global -> LDS copies (global_load_lds: lane i of the wave writes bytes
+// [base + size*i, base + size*(i+1)) of LDS, base taken from M0).  They are issued as inline
+// assembly on purpose: the compiler cannot tell the tile being filled from the tiles being
+// read, and would otherwise wait for every prefetch before the next LDS read.  Completion
+// is awaited explicitly (vmcnt) before the barrier that publishes a tile.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
+  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+// Workgroup barrier between two phases.  The LDS reads of the phase have been consumed by
+// the matrix instructions issued before it; the copies in flight keep going.  The
+// scheduling fences keep the compiler from moving any instruction across the barrier, which
+// would mix the two phases.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Wait until at most NOUT of this wave's copies into LDS are in flight (they complete in
+// issue order), then the barrier that publishes the completed ones.
+template <int NOUT>
+__device__ __forceinline__ void wait_dma_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NOUT) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
-// Direct global -> LDS copy of one 16 KB tile into the swizzled layout: wave w, instruction i
-// fills LDS chunks (4w + i) * 64 + lane, so each lane fetches the global chunk that belongs there.
-__device__ __forceinline__ void stage_tile(const uint8_t* gtile, uint8_t* ltile, int w, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int P = (4 * w + i) * 64 + lane;
-    const int row = P >> 3, c16 = swz_phys(row, P & 7);   // the XOR is an involution
-    __builtin_amdgcn_global_load_lds((const void*)(gtile + row * 128 + c16 * 16),
-                                     (lds_void*)(ltile + (4 * w + i) * 1024), 16, 0, 0);
-  }
+// Source offset (bytes, within a 16 KB tile) of the chunk a lane copies with instruction i
+// of wave w: the instruction fills LDS chunks (2w + i) * 64 + lane of the swizzled tile, so
+// each lane fetches the global chunk that belongs there (the XOR is an involution).
+__device__ __forceinline__ int stage_src(int w, int i, int lane) {
+  const int P = (2 * w + i) * 64 + lane;
+  const int row = P >> 3;
+  return row * 128 + (swz_phys(row, P & 7) << 4);
 }
 
 __device__ __forceinline__ v8i lds_frag32(const uint8_t* tile, int row, int c16) {
@@ -89,47 +124,100 @@ __device__ __forceinline__ v8i lds_frag32(const uint8_t* tile, int row, int c16)
 __device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
 }
-
+__device__ __forceinline__ v4f mfma_fp8_16(v8i a, v8i b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 __device__ __forceinline__ v16f mfma_bf16(v8s a, v8s b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
                                                  0, 0, 0);
 }
 
-typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
-constexpr v2bf BF16_ONES = {(__bf16)1.0f, (__bf16)1.0f};
-
-constexpr int MRING = 32;   // LDS ring of mean rows: two 16-tile groups (one being summed, one filling)
+// Constant A operand of the row-sum product D = A . B (16x16x128, FP8).  In that instruction
+// lane l holds row / column l%16 and k-block G = l/16 of A / B; the P bytes of lane l (query
+// l%32, key half l/32) therefore form k-block G of column n = l%16 with query n + 16 (G%2).
+// Rows 0 and 8 of A are ones on k-blocks 0 and 2 (query n), rows 4 and 12 on k-blocks 1 and
+// 3 (query n + 16), all else zero; lane l reads row 4 (l/16) in result register 0, which is
+// then the sum of its own query's 128 codes.  The codes are multiples of 2^-9 below 2^8, so
+// the sum (< 2^15) is exact in float32.
+__device__ __forceinline__ v8i rowsum_ones(int lane) {
+  const int i = lane & 15, G = lane >> 4;
+  const bool one = (G & 1) ? (i == 4 || i == 12) : (i == 0 || i == 8);
+  const int v = one ? 0x38383838 : 0;   // four E4M3 1.0
+  v8i r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = v;
+  return r;
+}
 
 }  // namespace
 
 template <bool NO_MEAN>
-__global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q,
+__global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q,
                                                   const uint8_t* __restrict__ Kq,
                                                   const float* __restrict__ sK,
                                                   const uint8_t* __restrict__ Rq,
                                                   const uint16_t* __restrict__ mu,
                                                   const float* __restrict__ sV, int N, int nqb,
-                                                  uint32_t G, float L, uint16_t* __restrict__ O) {
-  __shared__ __attribute__((aligned(1024))) uint8_t kt[2][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t rt[2][TILE_BYTES];
+                                                  int nwb, uint32_t G, float L, uint16_t* __restrict__ O) {
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[NBUF][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t rt[NBUF][TILE_BYTES];
   __shared__ __attribute__((aligned(256))) uint16_t mring[MRING][128];
-  __shared__ float red[4];
+  __shared__ float red[NWAVE];
 
-  const int t = threadIdx.x, w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, q = lane & 31, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int grp = w >> 2;
   const uint32_t item = xcd_remap(blockIdx.x, G);
-  const int bh = (int)(item / (uint32_t)nqb), qb = (int)(item % (uint32_t)nqb);
+  const int bh = (int)(item / (uint32_t)nwb), qb = 2 * (int)(item % (uint32_t)nwb) + grp;
+  const bool valid = qb < nqb;   // the last block of a head may have no second query block
   const int T = N / 128;
   const size_t headN = (size_t)bh * N;
-  const int qi = qb * 128 + w * 32 + q;
+  const int qi = (valid ? qb : nqb - 1) * 128 + (w & 3) * 32 + q;
   const uint8_t* Kh = Kq + headN * VC_D;
   const uint8_t* Rh = Rq + (size_t)bh * T * TILE_BYTES;
   const uint16_t* muh = mu + (size_t)bh * T * VC_D;
+  const float* sKh = sK + (size_t)bh * T;
 
-  // stage tile 0 (and clear the mean ring)
-  stage_tile(Kh, kt[0], w, lane);
-  stage_tile(Rh, rt[0], w, lane);
+  // this wave's share of every tile copy
+  const int so0 = stage_src(w, 0, lane), so1 = stage_src(w, 1, lane);
+  auto stage = [&](const uint8_t* gtile, uint8_t* ltile) {
+    dma16(gtile + so0, lds_addr(ltile + (2 * w) * 1024));
+    dma16(gtile + so1, lds_addr(ltile + (2 * w + 1) * 1024));
+  };
+  // Copies of step j: K tile j+D, R tile j+D-1 and mean row j+D-1 (D = NBUF-1), with tile
+  // indices clamped to T-1 so every step issues the same number of copies per wave (a
+  // clamped copy rewrites a buffer whose tile has been used up, or a mean-ring row whose
+  // rho is zero).
+  constexpr int D = NBUF - 1;
+  constexpr int NSET = 4;   // copies per wave and step, plus the mean row on wave 0
+  auto mean_row = [&](int i) {
+    if (!NO_MEAN && w == 0) dma4(muh + (size_t)i * VC_D + 2 * lane, lds_addr(&mring[i % MRING][0]));
+  };
+  auto clampT = [&](int i) { return i < T ? i : T - 1; };
+  auto issue = [&](int j) {
+    stage(Kh + (size_t)clampT(j + D) * TILE_BYTES, kt[(j + D) % NBUF]);
+    stage(Rh + (size_t)clampT(j + D - 1) * TILE_BYTES, rt[(j + D - 1) % NBUF]);
+    mean_row(clampT(j + D - 1));
+  };
+  // the end of phase 2j+1: the copies of step j-D+1 and before (K tile j+1, R tile j) have
+  // landed; the D-1 later steps may still be in flight
+  auto wait_step = [&]() {
+    if (!NO_MEAN && w == 0) wait_dma_barrier<(D - 1) * (NSET + 1)>();
+    else wait_dma_barrier<(D - 1) * NSET>();
+  };
+
+  // K tiles 0..D-1, R tiles and mean rows 0..D-2; clear the mean ring first (rows past the
+  // last tile multiply rho = 0 and must be finite)
   if (!NO_MEAN)
-    for (int i = t; i < MRING * 128 / 2; i += 256) ((uint32_t*)&mring[0][0])[i] = 0u;
+    for (int i = t; i < MRING * 128 / 2; i += NWAVE * 64) ((uint32_t*)&mring[0][0])[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < D; ++i) stage(Kh + (size_t)clampT(i) * TILE_BYTES, kt[i]);
+#pragma unroll
+  for (int i = 0; i < D - 1; ++i) {
+    stage(Rh + (size_t)clampT(i) * TILE_BYTES, rt[i]);
+    mean_row(clampT(i));
+  }
 
   // ---- prologue: Q L, its block scale sQ = 2^E (amax over the 128 x 128 block), E4M3 ----
   const uint16_t* qrow = Q + (headN + qi) * VC_D;
@@ -139,7 +227,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
   for (int c = 0; c < 2; ++c)
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const uint4 raw = *(const uint4*)(qrow + 64 * c + 32 * g + 8 * m);
+      const uint4 raw = *(const uint4*)(qrow + 64 * c + 32 * hl + 8 * m);
       const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -151,11 +239,9 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
     }
   amax = wave_max(amax);
   if (lane == 0) red[w] = amax;
-
   __syncthreads();   // red[] and the cleared ring
-  if (!NO_MEAN && w == 0)
-    __builtin_amdgcn_global_load_lds((const void*)(muh + 2 * lane), (lds_void*)&mring[0][0], 4, 0, 0);
-  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int r0 = 4 * grp;
+  amax = fmaxf(fmaxf(red[r0], red[r0 + 1]), fmaxf(red[r0 + 2], red[r0 + 3]));
   const int EQ = pow2_block_exponent(amax);
   const int sb = 127 + EQ;                         // E8M0 of sQ
   const float qinv = __builtin_ldexpf(1.0f, -EQ);  // exact
@@ -167,38 +253,83 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
       const float* x = &qs[32 * c + 4 * d4];
       qf[c][d4] = (int)e4m3x4(x[0] * qinv, x[1] * qinv, x[2] * qinv, x[3] * qinv);
     }
-  __builtin_amdgcn_s_waitcnt(0);   // tile 0 and its mean row have landed in LDS
-  __syncthreads();
+  wait_dma_barrier<0>();   // the first copies have landed
 
+  const v8i ones = rowsum_ones(lane);
   float b = 0.0f, l_run = 0.0f;   // b = 119.65 - m; set on the first tile
-  v16f bsplat = {};
-  float rho[8];                   // r of this group's tiles 8g .. 8g+7 (query q)
+  v16f bsplat = {};               // b in every element: the accumulator input of QK
+  float rho[8];                   // r of this group's tiles 8h .. 8h+7 (query q)
 #pragma unroll
   for (int k = 0; k < 8; ++k) rho[k] = 0.0f;
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = v16f{};
-
-  for (int j = 0; j < T; ++j) {
-    const int cur = j & 1;
-    if (j + 1 < T) {   // prefetch tile j+1 into the idle buffer (freed by the last barrier)
-      stage_tile(Kh + (size_t)(j + 1) * TILE_BYTES, kt[cur ^ 1], w, lane);
-      stage_tile(Rh + (size_t)(j + 1) * TILE_BYTES, rt[cur ^ 1], w, lane);
-      if (!NO_MEAN && w == 0)
-        __builtin_amdgcn_global_load_lds((const void*)(muh + (size_t)(j + 1) * VC_D + 2 * lane),
-                                         (lds_void*)&mring[(j + 1) % MRING][0], 4, 0, 0);
-    }
-
-    // t = a s + b from the matrix unit: S^T = Kq_j . Qq^T with block scales sK_j, sQ
-    const int sa = (int)((__float_as_uint(sK[(size_t)bh * T + j]) >> 23) & 0xFFu);  // E8M0 of sK_j
-    v16f s[4];
+  v16f s[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = mfma_fp8(lds_frag32(kt[cur], 32 * kb + q, 2 * g), qf[0], bsplat, sa, sb);
-      s[kb] = mfma_fp8(lds_frag32(kt[cur], 32 * kb + q, 4 + 2 * g), qf[1], s[kb], sa, sb);
-    }
+  for (int kb = 0; kb < 4; ++kb) s[kb] = v16f{};
+  v8i pw[2] = {};
+  v4f rs = {};
 
-    // running maximum (Eq. 1) in t's units
+  // Eq. 6's mean term of the 16-tile group that holds tile e: A += mu~^T rho
+  auto mean_group = [&](int e) {
+    v8s bhi, blo;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t hi = f32_to_bf16_rne(rho[k]);
+      bhi[k] = (short)hi;
+      blo[k] = (short)f32_to_bf16_rne(rho[k] - bf16_to_f32(hi));
+      rho[k] = 0.0f;
+    }
+    const int t0 = (e & ~15) + 8 * hl;   // first tile of this lane's K-slots
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      v8s am;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) am[k] = (short)mring[(t0 + k) % MRING][32 * db + q];
+      acc[db] = mfma_bf16(am, bhi, acc[db]);
+      acc[db] = mfma_bf16(am, blo, acc[db]);
+    }
+  };
+
+  // M(j): S^T of tile j (t = a s + b), then A += P R and the row sum of tile j-1
+  auto mphase = [&](int j, auto qk, auto pv) {
+    if constexpr (decltype(qk)::value) {
+      const uint8_t* kb_ = kt[j % NBUF];
+      const int sa = (int)((__float_as_uint(sKh[j]) >> 23) & 0xFFu);   // E8M0 of sK_j
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = mfma_fp8(lds_frag32(kb_, 32 * kb + q, 2 * hl), qf[0], bsplat, sa, sb);
+        s[kb] = mfma_fp8(lds_frag32(kb_, 32 * kb + q, 4 + 2 * hl), qf[1], s[kb], sa, sb);
+      }
+    }
+    if constexpr (decltype(pv)::value) {
+      const uint8_t* rb = rt[(j - 1) % NBUF];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          acc[db] = mfma_fp8(lds_frag32(rb, 32 * db + q, 4 * p + 2 * hl), pw[p], acc[db], 127, 127);
+      rs = mfma_fp8_16(ones, pw[0], v4f{});
+      rs = mfma_fp8_16(ones, pw[1], rs);
+      // the group that ended at tile j-2 has all its row sums in rho since V(j-1)
+      if (!NO_MEAN && j >= 2 && ((j - 2) & 15) == 15) mean_group(j - 2);
+    }
+  };
+  constexpr std::true_type Y{};
+  constexpr std::false_type X{};
+
+  // V(j): r of tile j-1 into l and rho, running maximum of tile j, its ExpCast codes
+  // (on the first tile rs is still zero, so the r insertion is a no-op)
+  auto vphase = [&](int j) {
+    {
+      const float r = rs[0];
+      l_run += r;
+      if (!NO_MEAN) {
+        const int jl = (j - 1) & 15;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rho[k] = (hl == (jl >> 3) && k == (jl & 7)) ? r : rho[k];
+      }
+    }
     float tm = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
@@ -226,14 +357,10 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
 #pragma unroll
       for (int i = 0; i < 16; ++i) bsplat[i] = b;
     }
-
-    // ExpCast Round + clip: one saturating RNE byte conversion per element, then the PV
-    // product of that key half.  Byte jj of the PV B-operand for key half p is element
-    // (kb = 2p + jj/16, i = jj%16) of S^T.
-    v8i pw[2];
-    float r = 0.0f;
+    // ExpCast Round + clip: one saturating RNE byte conversion per element.  Byte jj of the
+    // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
         const int kb = 2 * p + (wd >> 2), i0 = 4 * (wd & 3);
@@ -244,54 +371,67 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
         word = expcast_byte(s[kb][i0 + 3], 3, word);
         pw[p][wd] = (int)word;
       }
-      // O^T += Rq_j^T . P^T for this key half
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-        acc[db] = mfma_fp8(lds_frag32(rt[cur], 32 * db + q, 4 * p + 2 * g), pw[p], acc[db], 127, 127);
-      // row sum of the decoded codes (the values the PV instruction consumes): E4M3 values
-      // are exact in bf16, and a bf16 dot with (1, 1) adds a pair into the float32 sum
-#pragma unroll
-      for (int wd = 0; wd < 8; ++wd) {
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pw[p][wd], 1.0f, false),
-                                            BF16_ONES, r, false);
-        r = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(pw[p][wd], 1.0f, true),
-                                            BF16_ONES, r, false);
-      }
-    }
-    r = pair_sum(r);
-    l_run += r;
+  };
 
-    // Eq. 6: the rank-one mean term r mu~_j^T, collected per 16-tile group (see the header)
-    if (!NO_MEAN) {
-      const int jl = j & 15;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) rho[k] = (g == (jl >> 3) && k == (jl & 7)) ? r : rho[k];
-      if (jl == 15 || j == T - 1) {
-        v8s bhi, blo;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const uint32_t hi = f32_to_bf16_rne(rho[k]);
-          bhi[k] = (short)hi;
-          blo[k] = (short)f32_to_bf16_rne(rho[k] - bf16_to_f32(hi));
-          rho[k] = 0.0f;
-        }
-        const int t0 = (j & ~15) + 8 * g;   // first tile of this lane's K-slots
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          v8s am;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) am[k] = (short)mring[(t0 + k) % MRING][32 * db + q];
-          acc[db] = mfma_bf16(am, bhi, acc[db]);
-          acc[db] = mfma_bf16(am, blo, acc[db]);
-        }
-      }
+  // Phases 2j and 2j+1.  Copies of step j are issued at the start of phase 2j and awaited at
+  // the end of phase 2j+3: K tile j+2 replaces tile j-1 (last read in phase 2j-1), R tile j+1
+  // replaces tile j-2 (last read in phase 2j-1); they are first read in phases 2j+4 and 2j+4.
+  // Group 0 runs M(j) | V(j), group 1 V(j-1) | M(j); a wave without queries only copies.
+  if (!valid) {
+    for (int j = 0; j < T; ++j) {
+      issue(j);
+      phase_barrier();
+      wait_step();
     }
-
-    __builtin_amdgcn_s_waitcnt(0);   // the prefetched tile has landed before the barrier publishes it
-    __syncthreads();
+    phase_barrier();
+    wait_dma_barrier<0>();
+    return;
+  }
+  if (grp == 0) {
+    issue(0);
+    mphase(0, Y, X);
+    phase_barrier();
+    vphase(0);
+    wait_step();
+    for (int j = 1; j < T; ++j) {
+      issue(j);
+      mphase(j, Y, Y);
+      phase_barrier();
+      vphase(j);
+      wait_step();
+    }
+    mphase(T, X, Y);
+    phase_barrier();
+    wait_dma_barrier<0>();
+  } else {
+    issue(0);
+    phase_barrier();
+    mphase(0, Y, X);
+    wait_step();
+    for (int j = 1; j < T; ++j) {
+      issue(j);
+      vphase(j - 1);
+      phase_barrier();
+      mphase(j, Y, Y);
+      wait_step();
+    }
+    vphase(T - 1);
+    phase_barrier();
+    mphase(T, X, Y);
+    wait_dma_barrier<0>();
   }
 
-  // ---- epilogue: O = A * sV / l -> bf16 ----
+  // ---- epilogue: r of the last tile, the last mean group, O = A * sV / l -> bf16 ----
+  {
+    const float r = rs[0];
+    l_run += r;
+    if (!NO_MEAN) {
+      const int jl = (T - 1) & 15;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rho[k] = (hl == (jl >> 3) && k == (jl & 7)) ? r : rho[k];
+      mean_group(T - 1);
+    }
+  }
   const float inv_l = 1.0f / l_run;
   const float* sv = sV + (size_t)bh * VC_D;
   uint16_t* orow = O + (headN + qi) * VC_D;
@@ -299,7 +439,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd(const uint16_t* __restrict__ Q
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int ig = 0; ig < 4; ++ig) {
-      const int d0 = 32 * db + 8 * ig + 4 * g;
+      const int d0 = 32 * db + 8 * ig + 4 * hl;
       const float4 s4 = *(const float4*)(sv + d0);
       const uint32_t o0 = f32_to_bf16_rne(acc[db][4 * ig + 0] * s4.x * inv_l);
       const uint32_t o1 = f32_to_bf16_rne(acc[db][4 * ig + 1] * s4.y * inv_l);
@@ -313,11 +453,13 @@ hipError_t vc_launch_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float*
                               const uint8_t* Rq, const uint16_t* mu, const float* sV,
                               int BH, int N, float L, unsigned flags, uint16_t* O,
                               hipStream_t s) {
-  const int nqb = N / 128;
-  const uint32_t G = (uint32_t)BH * (uint32_t)nqb;
+  const int nqb = N / 128, nwb = (nqb + 1) / 2;
+  const uint32_t G = (uint32_t)BH * (uint32_t)nwb;
   if (flags & VC_ATTN_NO_MEAN)
-    hipLaunchKernelGGL(k_attn_fwd<true>, dim3(G), dim3(256), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, G, L, O);
+    hipLaunchKernelGGL(k_attn_fwd<true>, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb,
+                       G, L, O);
   else
-    hipLaunchKernelGGL(k_attn_fwd<false>, dim3(G), dim3(256), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, G, L, O);
+    hipLaunchKernelGGL(k_attn_fwd<false>, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb,
+                       G, L, O);
   return hipGetLastError();
 }
