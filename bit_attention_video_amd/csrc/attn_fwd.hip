@@ -6,12 +6,15 @@
 // in tiles of 128 (= B_v, so each tile has one key scale sK_j and one mean mu_j) through
 // LDS, filled by direct global->LDS copies that every wave shares.
 //
-// Ping-pong between the two groups.  Per tile a wave has a matrix part M(j) -- the QK
-// product of tile j, the PV product and the row sum of tile j-1 -- and a vector part V(j):
-// the running maximum and the ExpCast codes of tile j.  The groups run them in opposite
-// phases separated by workgroup barriers (group 0: M(j) | V(j), group 1: V(j-1) | M(j)).  A
-// SIMD holds one wave of each group, so while one of them keeps the matrix unit busy the
-// other does the vector work; with one workgroup per CU nothing else competes.
+// Ping-pong between the two groups.  Per tile a wave has a matrix part M(j) -- the PV
+// product and the row sum of tile j-1, then the QK product of tile j -- and a vector part
+// V(j): the running maximum and the ExpCast codes of tile j, which ends by reading the
+// residual fragments of the next PV product into registers.  The groups run them in
+// opposite phases separated by workgroup barriers (group 0: M(j) | V(j), group 1:
+// V(j-1) | M(j)).  A SIMD holds one wave of each group, so while one of them keeps the
+// matrix unit busy the other does the vector work; with one workgroup per CU nothing else
+// competes.  K and R tiles are copied three steps ahead into four-deep LDS rings; each wave
+// issues its share of the copies in its vector phase, away from the matrix instructions.
 //
 // Layouts.  Both products use the FP8 32x32x64 matrix instruction with the key index as the
 // reduction dimension of PV, computed transposed so one lane owns one query row:
@@ -39,8 +42,8 @@
 // Row sum (Eq. 6, r = sum of the decoded codes) on the matrix unit as well: a 16x16x128 FP8
 // product of a constant 0/1 operand with the P bytes returns each lane the sum of its
 // query's 128 codes (see rowsum_ones).  l += r.  The rank-one mean term r mu~_j^T runs on
-// the matrix unit too: each row keeps the r of the last 16 tiles (rho, rescaled with A when
-// the maximum grows), and once per 16 tiles A += mu~^T rho with the bf16 32x32x16
+// the matrix unit too: each row keeps the r of the current 16-tile group (rescaled with A
+// when the maximum grows), and once per group A += mu~^T rho with the bf16 32x32x16
 // instruction (mu~ is exact bf16; rho is split into bf16 hi + lo, 16 significant bits).
 // Epilogue: O = bf16(A * sV / l) (App. B: one multiply by sV serves both terms).
 #include "vc_common.h"
@@ -55,7 +58,7 @@ constexpr int TILE_BYTES = 128 * 128;
 constexpr float EC_C = 119.65f;    // 120 + beta, beta = -0.35 (Eq. 7)
 constexpr int NWAVE = 8;           // two groups of four waves
 constexpr int MRING = 32;          // LDS ring of mean rows: two 16-tile groups
-constexpr int NBUF = 2;            // K and R tile buffers each (prefetch depth NBUF - 1 tiles)
+constexpr int NBUF = 4;            // K and R tile buffers each (prefetch depth NBUF - 1 tiles)
 
 // Byte offset of 16-byte chunk c16 (0..7) of row `row` in a 128 x 128-byte LDS tile.  The
 // chunk index is XORed with (row % 8) ^ (row / 8 % 2): rows r..r+7 then hit 8 different
@@ -75,19 +78,26 @@ __device__ __forceinline__ float pair_max(float x) {
 // assembly on purpose: the compiler cannot tell the tile being filled from the tiles being
 // read, and would otherwise wait for every prefetch before the next LDS read.  Completion
 // is awaited explicitly (vmcnt) before the barrier that publishes a tile.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+// The global address is a per-lane 64-bit VGPR address.  (An SGPR base would need the five
+// wait states gfx9 requires between a vector write of an SGPR and a memory instruction that
+// reads it, which the compiler does not insert in front of inline assembly.)  The s_nop gives
+// the M0 write by the scalar unit a wait state before the copy reads it.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  const uint8_t* g = (const uint8_t*)gbase + voff;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds_base) {
-  asm volatile("global_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  const uint8_t* g = (const uint8_t*)gbase + voff;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
-// Workgroup barrier between two phases.  The LDS reads of the phase have been consumed by
-// the matrix instructions issued before it; the copies in flight keep going.  The
-// scheduling fences keep the compiler from moving any instruction across the barrier, which
-// would mix the two phases.
+// Workgroup barrier between two phases.  No LDS read needs to be complete here: every tile
+// buffer is rewritten only after the instructions that consume its reads, and the compiler
+// waits for a read before its consumer.  The copies in flight keep going.  The scheduling
+// fences keep the compiler from moving any instruction across the barrier, which would mix
+// the two phases.
 __device__ __forceinline__ void phase_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 // Wait until at most NOUT of this wave's copies into LDS are in flight (they complete in
@@ -95,8 +105,14 @@ __device__ __forceinline__ void phase_barrier() {
 template <int NOUT>
 __device__ __forceinline__ void wait_dma_barrier() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NOUT) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NOUT) : "memory");
   __builtin_amdgcn_sched_barrier(0);
+}
+// Pins a phase's results before the barrier that ends it: the compiler may not sink the
+// instructions that produce them into the next phase (no instruction is emitted).
+template <typename T>
+__device__ __forceinline__ void keep(T& x) {
+  asm volatile("" : "+v"(x));
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
@@ -139,13 +155,18 @@ __device__ __forceinline__ v16f mfma_bf16(v8s a, v8s b, v16f c) {
 // 3 (query n + 16), all else zero; lane l reads row 4 (l/16) in result register 0, which is
 // then the sum of its own query's 128 codes.  The codes are multiples of 2^-9 below 2^8, so
 // the sum (< 2^15) is exact in float32.
-__device__ __forceinline__ v8i rowsum_ones(int lane) {
+__device__ __forceinline__ int rowsum_ones_word(int lane) {
   const int i = lane & 15, G = lane >> 4;
   const bool one = (G & 1) ? (i == 4 || i == 12) : (i == 0 || i == 8);
-  const int v = one ? 0x38383838 : 0;   // four E4M3 1.0
+  return one ? 0x38383838 : 0;   // four E4M3 1.0
+}
+// The operand itself, rebuilt where it is used from the one register that holds its word
+// (opaque, so the compiler does not keep eight copies alive across the loop).
+__device__ __forceinline__ v8i rowsum_ones(int word) {
+  asm volatile("" : "+v"(word));
   v8i r;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) r[k] = v;
+  for (int k = 0; k < 8; ++k) r[k] = word;
   return r;
 }
 
@@ -162,6 +183,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   __shared__ __attribute__((aligned(1024))) uint8_t kt[NBUF][TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t rt[NBUF][TILE_BYTES];
   __shared__ __attribute__((aligned(256))) uint16_t mring[MRING][128];
+  // first-half row sums of each query row, and b at the time they were saved
+  __shared__ __attribute__((aligned(16))) float rsnap[NWAVE * 32][12];
   __shared__ float red[NWAVE];
 
   const int t = threadIdx.x, lane = t & 63, q = lane & 31, hl = lane >> 5;
@@ -178,11 +201,12 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   const uint16_t* muh = mu + (size_t)bh * T * VC_D;
   const float* sKh = sK + (size_t)bh * T;
 
-  // this wave's share of every tile copy
-  const int so0 = stage_src(w, 0, lane), so1 = stage_src(w, 1, lane);
-  auto stage = [&](const uint8_t* gtile, uint8_t* ltile) {
-    dma16(gtile + so0, lds_addr(ltile + (2 * w) * 1024));
-    dma16(gtile + so1, lds_addr(ltile + (2 * w + 1) * 1024));
+  // this wave's share of every tile copy: per-lane source offsets, LDS chunk offsets
+  const uint32_t so0 = stage_src(w, 0, lane), so1 = stage_src(w, 1, lane);
+  const uint32_t kt0 = lds_addr(&kt[0][0]) + 2 * w * 1024, rt0 = lds_addr(&rt[0][0]) + 2 * w * 1024;
+  auto stage = [&](const uint8_t* gtile, uint32_t lbase) {
+    dma16(gtile, so0, lbase);
+    dma16(gtile, so1, lbase + 1024);
   };
   // Copies of step j: K tile j+D, R tile j+D-1 and mean row j+D-1 (D = NBUF-1), with tile
   // indices clamped to T-1 so every step issues the same number of copies per wave (a
@@ -190,20 +214,22 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   // rho is zero).
   constexpr int D = NBUF - 1;
   constexpr int NSET = 4;   // copies per wave and step, plus the mean row on wave 0
+  const uint32_t mr0 = lds_addr(&mring[0][0]);
   auto mean_row = [&](int i) {
-    if (!NO_MEAN && w == 0) dma4(muh + (size_t)i * VC_D + 2 * lane, lds_addr(&mring[i % MRING][0]));
+    if (!NO_MEAN && w == 0) dma4(muh + (size_t)i * VC_D, 4 * lane, mr0 + (i % MRING) * 256);
   };
   auto clampT = [&](int i) { return i < T ? i : T - 1; };
   auto issue = [&](int j) {
-    stage(Kh + (size_t)clampT(j + D) * TILE_BYTES, kt[(j + D) % NBUF]);
-    stage(Rh + (size_t)clampT(j + D - 1) * TILE_BYTES, rt[(j + D - 1) % NBUF]);
+    stage(Kh + (size_t)clampT(j + D) * TILE_BYTES, kt0 + ((j + D) % NBUF) * TILE_BYTES);
+    stage(Rh + (size_t)clampT(j + D - 1) * TILE_BYTES, rt0 + ((j + D - 1) % NBUF) * TILE_BYTES);
     mean_row(clampT(j + D - 1));
   };
-  // the end of phase 2j+1: the copies of step j-D+1 and before (K tile j+1, R tile j) have
-  // landed; the D-1 later steps may still be in flight
+  // the end of phase 2j+1: the copies of step j-1 and before (up to K tile j+2, R tile j+1)
+  // have landed; step j may still be in flight.  So R tile j+1 is readable from phase 2j+2
+  // on, in time for V(j+1), which reads the fragments of PV(j+1) ahead of M(j+2).
   auto wait_step = [&]() {
-    if (!NO_MEAN && w == 0) wait_dma_barrier<(D - 1) * (NSET + 1)>();
-    else wait_dma_barrier<(D - 1) * NSET>();
+    if (!NO_MEAN && w == 0) wait_dma_barrier<(D - 2) * (NSET + 1)>();
+    else wait_dma_barrier<(D - 2) * NSET>();
   };
 
   // K tiles 0..D-1, R tiles and mean rows 0..D-2; clear the mean ring first (rows past the
@@ -212,10 +238,10 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     for (int i = t; i < MRING * 128 / 2; i += NWAVE * 64) ((uint32_t*)&mring[0][0])[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < D; ++i) stage(Kh + (size_t)clampT(i) * TILE_BYTES, kt[i]);
+  for (int i = 0; i < D; ++i) stage(Kh + (size_t)clampT(i) * TILE_BYTES, kt0 + i * TILE_BYTES);
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) {
-    stage(Rh + (size_t)clampT(i) * TILE_BYTES, rt[i]);
+    stage(Rh + (size_t)clampT(i) * TILE_BYTES, rt0 + i * TILE_BYTES);
     mean_row(clampT(i));
   }
 
@@ -255,12 +281,37 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     }
   wait_dma_barrier<0>();   // the first copies have landed
 
-  const v8i ones = rowsum_ones(lane);
+  const int ones_word = rowsum_ones_word(lane);
   float b = 0.0f, l_run = 0.0f;   // b = 119.65 - m; set on the first tile
-  v16f bsplat = {};               // b in every element: the accumulator input of QK
-  float rho[8];                   // r of this group's tiles 8h .. 8h+7 (query q)
+  // E8M0 exponent of sK of the tile of this wave's next QK product.  It is read in the vector
+  // phase before: a scalar load shares its wait counter with the LDS reads, and waiting for it
+  // inside the matrix phase would also wait for every fragment in flight.
+  auto e8m0_sk = [&](int i) { return (int)((__float_as_uint(sKh[i]) >> 23) & 0xFFu); };
+  int sa = e8m0_sk(0);
+  // Row sums of the current 16-tile group (query q), kept as a shift register: each tile's r
+  // enters rA[7] and pushes the older ones down.  After the group's 8th tile rA is saved to
+  // LDS (rsnap, with the b of that moment) and restarts; the saved half is rescaled once, at
+  // the group end, by 2^((b_end - b_snap)/8), the product of the maximum updates since.  At
+  // the group end the saved half holds tiles t0 .. t0+7 and rA[k] tile e-7+k (zero for tiles
+  // before t0+8): the bf16 instruction's K-slots of the lane halves 0 and 1.
+  float rA[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) rho[k] = 0.0f;
+  for (int k = 0; k < 8; ++k) rA[k] = 0.0f;
+  bool snapped = false;   // a first half of the current group is in rsnap
+  float* my_snap = &rsnap[w * 32 + q][0];
+  auto push_r = [&](float r, int e) {   // r of tile e
+#pragma unroll
+    for (int k = 0; k < 7; ++k) rA[k] = rA[k + 1];
+    rA[7] = r;
+    if ((e & 15) == 7) {
+      *(float4*)my_snap = make_float4(rA[0], rA[1], rA[2], rA[3]);
+      *(float4*)(my_snap + 4) = make_float4(rA[4], rA[5], rA[6], rA[7]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rA[k] = 0.0f;
+      my_snap[8] = b;
+      snapped = true;
+    }
+  };
   v16f acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) acc[db] = v16f{};
@@ -268,52 +319,100 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) s[kb] = v16f{};
   v8i pw[2] = {};
+  v8i rf[8];   // residual fragments of the next PV product, read at the end of the vector phase
+#pragma unroll
+  for (int i = 0; i < 8; ++i) rf[i] = v8i{};
   v4f rs = {};
 
-  // Eq. 6's mean term of the 16-tile group that holds tile e: A += mu~^T rho
+  // Eq. 6's mean term of the 16-tile group that ends with tile e: A += mu~^T rho
   auto mean_group = [&](int e) {
+    float rB[8];
+    if (snapped) {
+      const float4 s0 = *(const float4*)my_snap, s1 = *(const float4*)(my_snap + 4);
+      const float f = __builtin_amdgcn_exp2f(0.125f * (b - my_snap[8]));
+      rB[0] = s0.x * f; rB[1] = s0.y * f; rB[2] = s0.z * f; rB[3] = s0.w * f;
+      rB[4] = s1.x * f; rB[5] = s1.y * f; rB[6] = s1.z * f; rB[7] = s1.w * f;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rB[k] = 0.0f;
+    }
+    snapped = false;
     v8s bhi, blo;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const uint32_t hi = f32_to_bf16_rne(rho[k]);
+      const float rk = hl ? rA[k] : rB[k];
+      const uint32_t hi = f32_to_bf16_rne(rk);
       bhi[k] = (short)hi;
-      blo[k] = (short)f32_to_bf16_rne(rho[k] - bf16_to_f32(hi));
-      rho[k] = 0.0f;
+      blo[k] = (short)f32_to_bf16_rne(rk - bf16_to_f32(hi));
+      rA[k] = 0.0f;
     }
-    const int t0 = (e & ~15) + 8 * hl;   // first tile of this lane's K-slots
+    const int t0 = hl ? e - 7 : (e & ~15);   // tile of this lane's first K-slot
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       v8s am;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) am[k] = (short)mring[(t0 + k) % MRING][32 * db + q];
+      for (int k = 0; k < 8; ++k) am[k] = (short)mring[(t0 + k) & (MRING - 1)][32 * db + q];
       acc[db] = mfma_bf16(am, bhi, acc[db]);
       acc[db] = mfma_bf16(am, blo, acc[db]);
     }
   };
 
-  // M(j): S^T of tile j (t = a s + b), then A += P R and the row sum of tile j-1
+  // M(j): A += P R and the row sum of tile j-1, then S^T of tile j (t = a s + b).  All
+  // fragments of the residual tile are requested first and two key fragments after each PV
+  // instruction, so the matrix unit never waits for an LDS round trip inside the phase.
   auto mphase = [&](int j, auto qk, auto pv) {
-    if constexpr (decltype(qk)::value) {
+    constexpr bool QK = decltype(qk)::value, PV = decltype(pv)::value;
+    v8i kf[8];
+    if constexpr (QK) {
       const uint8_t* kb_ = kt[j % NBUF];
-      const int sa = (int)((__float_as_uint(sKh[j]) >> 23) & 0xFFu);   // E8M0 of sK_j
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = mfma_fp8(lds_frag32(kb_, 32 * kb + q, 2 * hl), qf[0], bsplat, sa, sb);
-        s[kb] = mfma_fp8(lds_frag32(kb_, 32 * kb + q, 4 + 2 * hl), qf[1], s[kb], sa, sb);
+        kf[2 * kb] = lds_frag32(kb_, 32 * kb + q, 2 * hl);
+        kf[2 * kb + 1] = lds_frag32(kb_, 32 * kb + q, 4 + 2 * hl);
       }
     }
-    if constexpr (decltype(pv)::value) {
-      const uint8_t* rb = rt[(j - 1) % NBUF];
+    if constexpr (PV) {
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-          acc[db] = mfma_fp8(lds_frag32(rb, 32 * db + q, 4 * p + 2 * hl), pw[p], acc[db], 127, 127);
+        for (int db = 0; db < 4; ++db) acc[db] = mfma_fp8(rf[4 * p + db], pw[p], acc[db], 127, 127);
+      const v8i ones = rowsum_ones(ones_word);
       rs = mfma_fp8_16(ones, pw[0], v4f{});
       rs = mfma_fp8_16(ones, pw[1], rs);
-      // the group that ended at tile j-2 has all its row sums in rho since V(j-1)
-      if (!NO_MEAN && j >= 2 && ((j - 2) & 15) == 15) mean_group(j - 2);
     }
+    if constexpr (QK) {
+      v16f bsplat;   // b in every element: the accumulator input, live until issued
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bsplat[i] = b;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = mfma_fp8(kf[2 * kb], qf[0], bsplat, sa, sb);
+        s[kb] = mfma_fp8(kf[2 * kb + 1], qf[1], s[kb], sa, sb);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) keep(s[kb]);
+    }
+    if constexpr (PV) keep(rs);
+    if constexpr (PV && QK) {
+      // key fragments two at a time behind the products, so at most four are in registers:
+      // PV 0-3 with K fragments 0-3, PV 4-7 and the row sums, QK 0-3 (chains 0, 1) with K
+      // fragments 4-7, QK 4-7
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+    // the group that ended at tile j-2 has all its row sums in rho since V(j-1)
+    if constexpr (PV)
+      if (!NO_MEAN && j >= 2 && ((j - 2) & 15) == 15) mean_group(j - 2);
   };
   constexpr std::true_type Y{};
   constexpr std::false_type X{};
@@ -324,11 +423,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     {
       const float r = rs[0];
       l_run += r;
-      if (!NO_MEAN) {
-        const int jl = (j - 1) & 15;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) rho[k] = (hl == (jl >> 3) && k == (jl & 7)) ? r : rho[k];
-      }
+      if (!NO_MEAN) push_r(r, j - 1);
     }
     float tm = -__builtin_inff();
 #pragma unroll
@@ -347,15 +442,13 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
         const float alpha = __builtin_amdgcn_exp2f(-0.125f * delta);
         l_run *= alpha;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) rho[k] *= alpha;
+        for (int k = 0; k < 8; ++k) rA[k] *= alpha;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
       }
       b -= delta;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bsplat[i] = b;
     }
     // ExpCast Round + clip: one saturating RNE byte conversion per element.  Byte jj of the
     // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
@@ -371,12 +464,25 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
         word = expcast_byte(s[kb][i0 + 3], 3, word);
         pw[p][wd] = (int)word;
       }
+    keep(pw[0]);
+    keep(pw[1]);
+    {   // the residual fragments of PV(j), the first products of M(j+1)
+      const uint8_t* rb = rt[j % NBUF];
+#pragma unroll
+      for (int p = 0; p < 2; ++p)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) rf[4 * p + db] = lds_frag32(rb, 32 * db + q, 4 * p + 2 * hl);
+    }
+    sa = e8m0_sk(j + 1 < T ? j + 1 : T - 1);   // for QK of tile j+1
+    keep(sa);
   };
 
-  // Phases 2j and 2j+1.  Copies of step j are issued at the start of phase 2j and awaited at
-  // the end of phase 2j+3: K tile j+2 replaces tile j-1 (last read in phase 2j-1), R tile j+1
-  // replaces tile j-2 (last read in phase 2j-1); they are first read in phases 2j+4 and 2j+4.
-  // Group 0 runs M(j) | V(j), group 1 V(j-1) | M(j); a wave without queries only copies.
+  // Phases 2j and 2j+1.  Group 0 runs M(j) | V(j), group 1 V(j-1) | M(j); each wave issues
+  // its copies of step j at the start of its vector phase (phase 2j+1 in group 0, 2j in group
+  // 1), keeping them out of the matrix-instruction stream, and every wave waits at the end of
+  // phase 2j+1 for step j-1 (K tile j+1, R tile j, first read in phase 2j+2).  Buffer reuse:
+  // step j overwrites K tile j-1 and R tile j-2, whose last reads were in phase 2j-1.
+  // A wave without queries only copies.
   if (!valid) {
     for (int j = 0; j < T; ++j) {
       issue(j);
@@ -388,15 +494,15 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     return;
   }
   if (grp == 0) {
-    issue(0);
     mphase(0, Y, X);
     phase_barrier();
+    issue(0);
     vphase(0);
     wait_step();
     for (int j = 1; j < T; ++j) {
-      issue(j);
       mphase(j, Y, Y);
       phase_barrier();
+      issue(j);
       vphase(j);
       wait_step();
     }
@@ -426,9 +532,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     const float r = rs[0];
     l_run += r;
     if (!NO_MEAN) {
-      const int jl = (T - 1) & 15;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) rho[k] = (hl == (jl >> 3) && k == (jl & 7)) ? r : rho[k];
+      push_r(r, T - 1);
       mean_group(T - 1);
     }
   }
