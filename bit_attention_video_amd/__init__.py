@@ -50,7 +50,7 @@ _SIGNATURES = {
     "vc_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
     "vc_test_expcast": (_I, [_P, _P, _Z, _P]),
     "vc_test_e4m3_encode": (_I, [_P, _P, _Z, _P]),
-    "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
+    "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "vc_test_label_sort": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
 }
 
@@ -206,8 +206,10 @@ def vc_test_kmeans_assign(V: torch.Tensor, C: torch.Tensor):
     _need(C, "C", torch.float32, (B, H, k, d))
     labels = torch.empty((B, H, N), dtype=torch.int32, device=V.device)
     dist = torch.empty((B, H, N), dtype=torch.float32, device=V.device)
-    _check(lib().vc_test_kmeans_assign(_ptr(V), _ptr(C), B, H, N, d, k, _ptr(labels), _ptr(dist), _stream()),
-           "vc_test_kmeans_assign")
+    nws = lib().vc_group_workspace_size(B, H, N, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=V.device)
+    _check(lib().vc_test_kmeans_assign(_ptr(V), _ptr(C), B, H, N, d, k, _ptr(labels), _ptr(dist), _ptr(ws),
+                                       nws, _stream()), "vc_test_kmeans_assign")
     return labels, dist
 
 

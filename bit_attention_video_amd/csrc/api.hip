@@ -31,12 +31,16 @@ int check_shape(int B, int H, int N, int d) {
 
 }  // namespace
 
-vc_group_ws vc_group_ws_layout(int BH, int N) {
+vc_group_ws vc_group_ws_layout(int BH, int N, int k) {
   vc_group_ws L;
   size_t nblk = (size_t)(N + VC_SORT_TILE - 1) / VC_SORT_TILE;
+  size_t kpad = (size_t)((k + 31) & ~31);
   size_t off = 0;
   L.hist = off;  off = align256(off + (size_t)BH * nblk * 256 * sizeof(int32_t));
   L.jpart = off; off = align256(off + (size_t)BH * ((size_t)(N + 255) / 256) * sizeof(double));
+  L.chi = off;   off = align256(off + (size_t)BH * kpad * VC_HEAD_DIM * sizeof(uint16_t));
+  L.clo = off;   off = align256(off + (size_t)BH * kpad * VC_HEAD_DIM * sizeof(uint16_t));
+  L.cnorm = off; off = align256(off + (size_t)BH * kpad * sizeof(float));
   L.total = off;
   return L;
 }
@@ -73,9 +77,9 @@ const char* vc_strerror(int status) {
 int vc_last_hip_error(void) { return g_last_hip_error; }
 
 size_t vc_group_workspace_size(int B, int H, int N, int k) {
-  (void)k;
   if (B <= 0 || H <= 0 || N <= 0) return 0;
-  return vc_group_ws_layout(B * H, N).total;
+  if (k < 1 || k > VC_MAX_K) k = VC_MAX_K;   // an invalid k is rejected by the call itself
+  return vc_group_ws_layout(B * H, N, k).total;
 }
 
 size_t vc_demean_quant_workspace_size(int B, int H, int N) {
@@ -94,11 +98,14 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
   if (k < 1 || k > VC_MAX_K || k > N) return VC_ERR_K;
   if (iters < 1) return VC_ERR_ITERS;
   int BH = B * H;
-  vc_group_ws L = vc_group_ws_layout(BH, N);
+  vc_group_ws L = vc_group_ws_layout(BH, N, k);
   if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
   char* w = (char*)ws;
   int32_t* hist = (int32_t*)(w + L.hist);
   double* jpart = (double*)(w + L.jpart);
+  uint16_t* chi = (uint16_t*)(w + L.chi);
+  uint16_t* clo = (uint16_t*)(w + L.clo);
+  float* cnorm = (float*)(w + L.cnorm);
   hipError_t e = hipSuccess;
   if (C_init) {
     if (C_init != C_out)
@@ -109,7 +116,8 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
   }
   if (e != hipSuccess) return hip_status(e);
   for (int it = 0; it < iters; ++it) {
-    if ((e = vc_launch_kmeans_assign(V, C_out, BH, N, k, labels, nullptr, stream)) != hipSuccess)
+    if ((e = vc_launch_kmeans_assign(V, C_out, BH, N, k, labels, nullptr, chi, clo, cnorm, stream)) !=
+        hipSuccess)
       return hip_status(e);
     if ((e = vc_launch_label_sort(labels, BH, N, k, hist, perm, offsets, stream)) != hipSuccess)
       return hip_status(e);
@@ -171,13 +179,18 @@ int vc_test_e4m3_encode(const float* x, uint8_t* codes, size_t n, hipStream_t st
 }
 
 int vc_test_kmeans_assign(const uint16_t* V, const float* C, int B, int H, int N, int d, int k,
-                          int32_t* labels, float* mindist, hipStream_t stream) {
+                          int32_t* labels, float* mindist, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
   int st = check_shape(B, H, N, d);
   if (st < 0) return st;
   if (st == 1) return VC_OK;
-  if (!V || !C || !labels) return VC_ERR_NULL;
+  if (!V || !C || !labels || !ws) return VC_ERR_NULL;
   if (k < 1 || k > VC_MAX_K || k > N) return VC_ERR_K;
-  return hip_status(vc_launch_kmeans_assign(V, C, B * H, N, k, labels, mindist, stream));
+  vc_group_ws L = vc_group_ws_layout(B * H, N, k);
+  if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
+  char* w = (char*)ws;
+  return hip_status(vc_launch_kmeans_assign(V, C, B * H, N, k, labels, mindist, (uint16_t*)(w + L.chi),
+                                            (uint16_t*)(w + L.clo), (float*)(w + L.cnorm), stream));
 }
 
 int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_t* perm,
@@ -187,7 +200,7 @@ int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_
   if (st == 1) return VC_OK;
   if (!labels || !perm || !offsets || !ws) return VC_ERR_NULL;
   if (k < 1 || k > VC_MAX_K || k > N) return VC_ERR_K;
-  vc_group_ws L = vc_group_ws_layout(B * H, N);
+  vc_group_ws L = vc_group_ws_layout(B * H, N, k);
   if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
   return hip_status(vc_launch_label_sort(labels, B * H, N, k, (int32_t*)((char*)ws + L.hist),
                                          perm, offsets, stream));

@@ -6,7 +6,8 @@
 //             on the bf16 matrix cores: v is exactly bf16, c is split into bf16 hi + lo parts
 //             (16 significant bits), two MFMAs accumulate in float32.  dist = ||c||^2 - 2 v.c;
 //             each lane keeps the best of its 16 centroids per block, one cross-lane exchange
-//             finishes the argmin.
+//             finishes the argmin.  A prep kernel splits the centroids and computes ||c||^2
+//             once per (b, h) and iteration; every assign workgroup copies them into LDS.
 //   update    c_c = float32(sum of its rows / count), the sum in float64 in a fixed order over
 //             the rows of cluster c in sorted order (perm, offsets from the label sort); an
 //             empty cluster keeps its centroid.
@@ -14,7 +15,7 @@
 #include "vc_common.h"
 #include "vc_internal.h"
 
-constexpr int KM_TOK_WG = 512;   // tokens per assign workgroup (4 waves x 4 groups x 32)
+constexpr int KM_TOK_WG = 1024;  // tokens per assign workgroup (4 waves x 8 groups x 32)
 constexpr int KM_ROW = 136;      // LDS row stride in bf16: 128 + 8 pad = 272 bytes
 
 __global__ __launch_bounds__(128) void k_kmeans_init(const uint16_t* __restrict__ V, int N, int k,
@@ -24,31 +25,53 @@ __global__ __launch_bounds__(128) void k_kmeans_init(const uint16_t* __restrict_
   C[((size_t)bh * k + c) * VC_D + e] = bf16_to_f32(V[((size_t)bh * N + row) * VC_D + e]);
 }
 
+// Centroids as bf16 hi + lo rows [kpad][128] and their squared norms (float32, summed over the
+// channels in order; padding rows get +inf so they never win).
+__global__ __launch_bounds__(128) void k_kmeans_prep(const float* __restrict__ C, int k, int kpad,
+                                                     uint16_t* __restrict__ chi, uint16_t* __restrict__ clo,
+                                                     float* __restrict__ cn) {
+  const int c = blockIdx.x, bh = blockIdx.y, e = threadIdx.x;
+  const size_t o = ((size_t)bh * kpad + c) * VC_D + e;
+  if (c >= k) {   // padding row (uniform per block)
+    chi[o] = 0;
+    clo[o] = 0;
+    if (e == 0) cn[(size_t)bh * kpad + c] = __builtin_inff();
+    return;
+  }
+  const float* crow = C + ((size_t)bh * k + c) * VC_D;
+  const float x = crow[e];
+  const uint32_t hi = f32_to_bf16_rne(x);
+  const uint32_t lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
+  chi[o] = (uint16_t)hi;
+  clo[o] = (uint16_t)lo;
+  if (e == 0) {
+    float s = 0.0f;
+    for (int i = 0; i < VC_D; ++i) s = fmaf(crow[i], crow[i], s);
+    cn[(size_t)bh * kpad + c] = s;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restrict__ V,
-                                                       const float* __restrict__ C, int N, int k,
-                                                       int kpad, int32_t* __restrict__ labels,
+                                                       const uint16_t* __restrict__ phi,
+                                                       const uint16_t* __restrict__ plo,
+                                                       const float* __restrict__ pcn, int N, int kpad,
+                                                       int32_t* __restrict__ labels,
                                                        float* __restrict__ mindist) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   uint16_t* chi = (uint16_t*)smem;                     // [kpad][KM_ROW]
   uint16_t* clo = chi + (size_t)kpad * KM_ROW;         // [kpad][KM_ROW]
   float* cn = (float*)(clo + (size_t)kpad * KM_ROW);   // [kpad]
   const int bh = blockIdx.y, t = threadIdx.x;
-  const float* Cb = C + (size_t)bh * k * VC_D;
 
-  for (int i = t; i < kpad * VC_D; i += 256) {
-    const int c = i >> 7, e = i & 127;
-    const float x = c < k ? Cb[i] : 0.0f;
-    const uint32_t hi = f32_to_bf16_rne(x);
-    const uint32_t lo = f32_to_bf16_rne(x - bf16_to_f32(hi));
-    chi[c * KM_ROW + e] = (uint16_t)hi;
-    clo[c * KM_ROW + e] = (uint16_t)lo;
+  // copy the prepared centroids into the padded LDS rows (16-byte chunks)
+  const uint4* ghi = (const uint4*)(phi + (size_t)bh * kpad * VC_D);
+  const uint4* glo = (const uint4*)(plo + (size_t)bh * kpad * VC_D);
+  for (int i = t; i < kpad * (VC_D / 8); i += 256) {
+    const int c = i >> 4, ch = i & 15;
+    *(uint4*)(chi + c * KM_ROW + 8 * ch) = ghi[i];
+    *(uint4*)(clo + c * KM_ROW + 8 * ch) = glo[i];
   }
-  for (int c = t; c < kpad; c += 256) {
-    float s = 0.0f;
-    if (c < k)
-      for (int e = 0; e < VC_D; ++e) s = fmaf(Cb[c * VC_D + e], Cb[c * VC_D + e], s);
-    cn[c] = c < k ? s : __builtin_inff();
-  }
+  for (int c = t; c < kpad; c += 256) cn[c] = pcn[(size_t)bh * kpad + c];
   __syncthreads();
 
   const int w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
@@ -104,37 +127,39 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restric
   }
 }
 
-// Centroid update: one workgroup per (cluster, b*h); 16 row streams x 32 channel quads.
+// Centroid update: one workgroup per (cluster, b*h); 32 row streams x 16 lanes of 8 channels.
+// The sums are float64 sums of bf16 values (exact unless a cluster's values span more than
+// about 45 binary orders of magnitude), reduced in a fixed order.
 __global__ __launch_bounds__(512) void k_kmeans_update(const uint16_t* __restrict__ V,
                                                        const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ offsets,
                                                        int N, int k, float* __restrict__ C) {
-  __shared__ double part[16][VC_D];
+  __shared__ double part[32][VC_D];
   const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
-  const int q4 = t & 31, st = t >> 5;
+  const int l8 = t & 15, st = t >> 4;
   const int beg = offsets[(size_t)bh * (k + 1) + c], end = offsets[(size_t)bh * (k + 1) + c + 1];
   if (end <= beg) return;  // empty cluster keeps its centroid (uniform branch)
   const int32_t* pb = perm + (size_t)bh * N;
-  const uint16_t* Vb = V + (size_t)bh * N * VC_D + 4 * q4;
-  double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+  const uint16_t* Vb = V + (size_t)bh * N * VC_D + 8 * l8;
+  double a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll 4
-  for (int p = beg + st; p < end; p += 16) {
+  for (int p = beg + st; p < end; p += 32) {
     const int tok = pb[p];
-    const uint2 raw = *(const uint2*)(Vb + (size_t)tok * VC_D);
-    a0 += (double)bf16_to_f32(raw.x & 0xFFFFu);
-    a1 += (double)bf16_to_f32(raw.x >> 16);
-    a2 += (double)bf16_to_f32(raw.y & 0xFFFFu);
-    a3 += (double)bf16_to_f32(raw.y >> 16);
+    const uint4 raw = *(const uint4*)(Vb + (size_t)tok * VC_D);
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] += (double)bf16_to_f32(wd[i] & 0xFFFFu);
+      a[2 * i + 1] += (double)bf16_to_f32(wd[i] >> 16);
+    }
   }
-  part[st][4 * q4 + 0] = a0;
-  part[st][4 * q4 + 1] = a1;
-  part[st][4 * q4 + 2] = a2;
-  part[st][4 * q4 + 3] = a3;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[st][8 * l8 + i] = a[i];
   __syncthreads();
   if (t < VC_D) {
     double s = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s += part[i][t];
+    for (int i = 0; i < 32; ++i) s += part[i][t];
     C[((size_t)bh * k + c) * VC_D + t] = (float)(s / (double)(end - beg));
   }
 }
@@ -184,15 +209,17 @@ hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float*
 }
 
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
-                                   int32_t* labels, float* mindist, hipStream_t s) {
+                                   int32_t* labels, float* mindist, uint16_t* chi, uint16_t* clo,
+                                   float* cn, hipStream_t s) {
   const int kpad = (k + 31) & ~31;
+  hipLaunchKernelGGL(k_kmeans_prep, dim3(kpad, BH), dim3(128), 0, s, C, k, kpad, chi, clo, cn);
   const size_t lds = (size_t)2 * kpad * KM_ROW * sizeof(uint16_t) + (size_t)kpad * sizeof(float);
   hipError_t e = hipFuncSetAttribute((const void*)k_kmeans_assign,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nblk = (N + KM_TOK_WG - 1) / KM_TOK_WG;
-  hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(256), lds, s, V, C, N, k, kpad, labels,
-                     mindist);
+  hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(256), lds, s, V, (const uint16_t*)chi,
+                     (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist);
   return hipGetLastError();
 }
 

@@ -10,9 +10,11 @@
 struct vc_group_ws {
   size_t hist;      // int32 [BH][nblk][256] per-block label histograms, then scatter bases
   size_t jpart;     // float64 [BH][N/256] objective partial sums
+  size_t chi, clo;  // bf16 [BH][kpad][128] centroids split into hi + lo parts (kpad = k to 32)
+  size_t cnorm;     // float32 [BH][kpad] squared centroid norms
   size_t total;
 };
-vc_group_ws vc_group_ws_layout(int BH, int N);
+vc_group_ws vc_group_ws_layout(int BH, int N, int k);
 
 // Workspace layout of the demean/quantise call.
 struct vc_dq_ws {
@@ -32,7 +34,8 @@ hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStre
 
 hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float* C, hipStream_t s);
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
-                                   int32_t* labels, float* mindist, hipStream_t s);
+                                   int32_t* labels, float* mindist, uint16_t* chi, uint16_t* clo,
+                                   float* cn, hipStream_t s);
 hipError_t vc_launch_kmeans_update(const uint16_t* V, const int32_t* perm, const int32_t* offsets,
                                    int BH, int N, int k, float* C, hipStream_t s);
 hipError_t vc_launch_kmeans_objective(const uint16_t* V, const int32_t* labels, const float* C,

@@ -163,9 +163,10 @@ int vc_test_e4m3_encode(const float* x, uint8_t* codes, size_t n, hipStream_t st
 
 /* One k-means assignment with given centroids C [B,H,k,d] float32 (the assign step of
  * vc_vsmooth_group): labels int32 [B,H,N]; mindist float32 [B,H,N] (||v - c_z||^2 as the
- * kernel computed it, may be NULL). */
+ * kernel computed it, may be NULL).  ws: at least vc_group_workspace_size(B,H,N,k) bytes. */
 int vc_test_kmeans_assign(const uint16_t* V, const float* C, int B, int H, int N, int d, int k,
-                          int32_t* labels, float* mindist, hipStream_t stream);
+                          int32_t* labels, float* mindist, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* Stable counting sort of labels int32 [B,H,N] with values in [0,k): perm, offsets as in
  * vc_vsmooth_group.  ws: at least vc_group_workspace_size(B,H,N,k) bytes. */

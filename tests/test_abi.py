@@ -100,7 +100,9 @@ def test_hook_argument_errors():
     assert lib.vc_test_expcast(None, None, 0, None) == S["VC_OK"]
     assert lib.vc_test_expcast(None, FAKE, 10, None) == S["VC_ERR_NULL"]
     assert lib.vc_test_e4m3_encode(FAKE, None, 10, None) == S["VC_ERR_NULL"]
-    assert lib.vc_test_kmeans_assign(FAKE, FAKE, 1, 1, 256, 128, 300, FAKE, None, None) == S["VC_ERR_K"]
+    assert lib.vc_test_kmeans_assign(FAKE, FAKE, 1, 1, 256, 128, 300, FAKE, None, FAKE, 1 << 30, None) == S["VC_ERR_K"]
+    assert lib.vc_test_kmeans_assign(FAKE, FAKE, 1, 1, 256, 128, 8, FAKE, None, None, 0, None) == S["VC_ERR_NULL"]
+    assert lib.vc_test_kmeans_assign(FAKE, FAKE, 1, 1, 256, 128, 8, FAKE, None, FAKE, 16, None) == S["VC_ERR_WORKSPACE"]
     ws = lib.vc_group_workspace_size(1, 1, 256, 4)
     assert lib.vc_test_label_sort(FAKE, 1, 1, 256, 4, FAKE, FAKE, FAKE, ws - 1, None) == S["VC_ERR_WORKSPACE"]
 
