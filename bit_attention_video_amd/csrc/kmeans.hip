@@ -15,7 +15,7 @@
 #include "vc_common.h"
 #include "vc_internal.h"
 
-constexpr int KM_TOK_WG = 1024;  // tokens per assign workgroup (4 waves x 8 groups x 32)
+constexpr int KM_TOK_WG = 1024;  // tokens per assign workgroup (4 waves x 4 groups x 64)
 constexpr int KM_ROW = 136;      // LDS row stride in bf16: 128 + 8 pad = 272 bytes
 
 __global__ __launch_bounds__(128) void k_kmeans_init(const uint16_t* __restrict__ V, int N, int k,
@@ -74,56 +74,84 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restric
   for (int c = t; c < kpad; c += 256) cn[c] = pcn[(size_t)bh * kpad + c];
   __syncthreads();
 
+  // Each wave takes 64 tokens per group (two 32-token halves sharing every centroid fragment);
+  // the rows of the next group are loaded while the current one is computed.  Token indices
+  // past N are clamped (their labels are not written).
   const int w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
   const int nblk = kpad >> 5;
-  for (int grp = 0; grp < KM_TOK_WG / 128; ++grp) {
-    const int tok = blockIdx.x * KM_TOK_WG + grp * 128 + w * 32 + q;
-    const bool valid = tok < N;
-    v8s vb[8];
-    float vn = 0.0f;
-    const uint16_t* vrow = V + ((size_t)bh * N + (valid ? tok : 0)) * VC_D;
+  const uint16_t* Vb = V + (size_t)bh * N * VC_D + 8 * g;
+  auto tok_of = [&](int grp, int h) { return blockIdx.x * KM_TOK_WG + grp * 256 + w * 64 + h * 32 + q; };
+  auto load_rows = [&](int grp, v8s (&vb)[2][8]) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      uint4 raw = valid ? *(const uint4*)(vrow + 16 * c + 8 * g) : make_uint4(0, 0, 0, 0);
-      vb[c] = __builtin_bit_cast(v8s, raw);
-      const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+    for (int h = 0; h < 2; ++h) {
+      const int tok = tok_of(grp, h);
+      const uint16_t* vrow = Vb + (size_t)(tok < N ? tok : N - 1) * VC_D;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float a = bf16_to_f32(wds[j] & 0xFFFFu), b = bf16_to_f32(wds[j] >> 16);
-        vn = fmaf(a, a, vn);
-        vn = fmaf(b, b, vn);
-      }
+      for (int c = 0; c < 8; ++c) vb[h][c] = __builtin_bit_cast(v8s, *(const uint4*)(vrow + 16 * c));
     }
-    float best = __builtin_inff();
-    int bi = 0;
+  };
+  v8s vcur[2][8], vnext[2][8];
+  load_rows(0, vcur);
+#pragma unroll
+  for (int grp = 0; grp < KM_TOK_WG / 256; ++grp) {
+    if (grp + 1 < KM_TOK_WG / 256) load_rows(grp + 1, vnext);
+    float best[2] = {__builtin_inff(), __builtin_inff()};
+    int bi[2] = {0, 0};
     for (int cb = 0; cb < nblk; ++cb) {
-      v16f acc = {};
+      v16f acc[2] = {v16f{}, v16f{}};
       const uint16_t* hrow = chi + (cb * 32 + q) * KM_ROW + 8 * g;
       const uint16_t* lrow = clo + (cb * 32 + q) * KM_ROW + 8 * g;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const v8s ah = *(const v8s*)(hrow + 16 * c);
-        const v8s al = *(const v8s*)(lrow + 16 * c);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, ah),
-                                                      __builtin_bit_cast(v8bf, vb[c]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, al),
-                                                      __builtin_bit_cast(v8bf, vb[c]), acc, 0, 0, 0);
-      }
+        const v8bf ah = __builtin_bit_cast(v8bf, *(const v8s*)(hrow + 16 * c));
+        const v8bf al = __builtin_bit_cast(v8bf, *(const v8s*)(lrow + 16 * c));
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int ci = cb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        const float dist = fmaf(-2.0f, acc[i], cn[ci]);
-        if (dist < best) { best = dist; bi = ci; }
+        for (int h = 0; h < 2; ++h) {
+          const v8bf b = __builtin_bit_cast(v8bf, vcur[h][c]);
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[h], 0, 0, 0);
+          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[h], 0, 0, 0);
+        }
+      }
+      // candidates of this lane in increasing index order: ci = 32 cb + 8 m + 4 g + r
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 n4 = *(const float4*)(cn + cb * 32 + 8 * m + 4 * g);
+        const float nn[4] = {n4.x, n4.y, n4.z, n4.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ci = cb * 32 + 8 * m + 4 * g + r;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float dist = fmaf(-2.0f, acc[h][4 * m + r], nn[r]);
+            if (dist < best[h]) { best[h] = dist; bi[h] = ci; }
+          }
+        }
       }
     }
-    const float ob = __shfl_xor(best, 32, 64);
-    const int oi = __shfl_xor(bi, 32, 64);
-    if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-    vn += __shfl_xor(vn, 32, 64);
-    if (valid && g == 0) {
-      labels[(size_t)bh * N + tok] = bi;
-      if (mindist) mindist[(size_t)bh * N + tok] = vn + best;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float ob = __shfl_xor(best[h], 32, 64);
+      const int oi = __shfl_xor(bi[h], 32, 64);
+      if (ob < best[h] || (ob == best[h] && oi < bi[h])) { best[h] = ob; bi[h] = oi; }
+      const int tok = tok_of(grp, h);
+      if (tok < N && g == 0) labels[(size_t)bh * N + tok] = bi[h];
+      if (mindist) {   // ||v||^2 + the best distance term (test output only)
+        float vn = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = bf16_to_f32((uint16_t)vcur[h][c][e]);
+            vn = fmaf(x, x, vn);
+          }
+        vn += __shfl_xor(vn, 32, 64);
+        if (tok < N && g == 0) mindist[(size_t)bh * N + tok] = vn + best[h];
+      }
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) vcur[h][c] = vnext[h][c];
   }
 }
 
@@ -142,15 +170,26 @@ __global__ __launch_bounds__(512) void k_kmeans_update(const uint16_t* __restric
   const int32_t* pb = perm + (size_t)bh * N;
   const uint16_t* Vb = V + (size_t)bh * N * VC_D + 8 * l8;
   double a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 4
-  for (int p = beg + st; p < end; p += 32) {
-    const int tok = pb[p];
-    const uint4 raw = *(const uint4*)(Vb + (size_t)tok * VC_D);
-    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  // stream st takes the rows beg+st, beg+st+32, ...; its 16 lanes fetch the next 16 row
+  // indices at once and share them, so 16 row loads are in flight per stream
+  for (int p0 = beg + st; p0 < end; p0 += 32 * 16) {
+    const int pl = p0 + 32 * l8;
+    const int mytok = pl < end ? pb[pl] : 0;
+    const int n = (end - p0 + 31) / 32 < 16 ? (end - p0 + 31) / 32 : 16;   // rows of this batch
+    uint4 raw[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[2 * i] += (double)bf16_to_f32(wd[i] & 0xFFFFu);
-      a[2 * i + 1] += (double)bf16_to_f32(wd[i] >> 16);
+    for (int i = 0; i < 16; ++i) {
+      const int tok = __shfl(mytok, (t & 48) + i, 64);   // lane i of this 16-lane stream
+      raw[i] = i < n ? *(const uint4*)(Vb + (size_t)tok * VC_D) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        a[2 * e] += (double)bf16_to_f32(wd[e] & 0xFFFFu);
+        a[2 * e + 1] += (double)bf16_to_f32(wd[e] >> 16);
+      }
     }
   }
 #pragma unroll
