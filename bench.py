@@ -48,7 +48,7 @@ def attn_flops(B, H, N, d):
     return 4.0 * B * H * N * N * d
 
 
-def cpu_baseline(cfg, Q, K, V, perm0, rows=256):
+def cpu_baseline(cfg, Q, K, V, perm0, rows=16384):
     """The oracle's emulated VC attention for `rows` query rows of head 0 (full N keys)."""
     from oracle import attention as T
     from oracle import formats as F
@@ -144,6 +144,20 @@ def main():
     log(f"step {ms_step:.2f} ms: group {t_group:.2f} ms, demean_quant {t_dq:.3f} ms, attn {t_attn:.2f} ms")
     assert torch.isfinite(O.float()).all(), "non-finite attention output"
 
+    # the same attention with P by exp-then-cast (v_exp_f32 + FP8 conversion) instead of ExpCast,
+    # the comparator of the pages' Table 4, timed the same way on the same operands
+    def time_attn(reps, **kw):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"], out=O, **kw)
+        e0.record()
+        for _ in range(reps):
+            vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"], out=O, **kw)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+    t_etc = time_attn(3, exp_then_cast=True)
+    log(f"attention with exp-then-cast P: {t_etc:.2f} ms (ExpCast {t_attn:.2f} ms)")
+
     if args.attn_only_iters:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -185,6 +199,8 @@ def main():
         "group_ms": round(t_group, 4), "demean_quant_ms": round(t_dq, 4),
         "demean_quant_gbs": round(dq_bytes / (t_dq * 1e-3) / 1e9, 1),
         "vsmooth_over_attn": {k2: round(v2, 4) for k2, v2 in amort.items()},
+        "p_path": {"expcast_ms": round(t_attn, 4), "exp_then_cast_ms": round(t_etc, 4),
+                   "expcast_speedup": round(t_etc / t_attn, 4)},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -25,11 +25,12 @@ import torch
 __all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_attn_fwd",
            "vc_attention", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
            "vc_test_label_sort", "rq_tiled_to_natural", "rq_natural_to_tiled", "LIB_PATH",
-           "VC_ATTN_NO_MEAN", "VC_DQ_NO_DEMEAN", "STATUS"]
+           "VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_DQ_NO_DEMEAN", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvcattn.so")
 
 VC_ATTN_NO_MEAN = 0x1
+VC_ATTN_EXP_THEN_CAST = 0x2
 VC_DQ_NO_DEMEAN = 0x1
 STATUS = {"VC_OK": 0, "VC_ERR_NULL": -1, "VC_ERR_SHAPE": -2, "VC_ERR_K": -3, "VC_ERR_ITERS": -4,
           "VC_ERR_WORKSPACE": -5, "VC_ERR_OVERFLOW": -6, "VC_ERR_FLAGS": -7, "VC_ERR_HIP": -8}
@@ -159,8 +160,9 @@ def vc_vsmooth_demean_quant(K: torch.Tensor, V: torch.Tensor, perm: Optional[tor
 
 def vc_attn_fwd(Q: torch.Tensor, Kq: torch.Tensor, sK: torch.Tensor, Rq: torch.Tensor,
                 mu: Optional[torch.Tensor], sV: torch.Tensor, softmax_scale: float = 0.0,
-                no_mean: bool = False, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """FP8 attention with ExpCast-FP8 and the online mean restore (Eq. 1, 6, 7)."""
+                no_mean: bool = False, out: Optional[torch.Tensor] = None,
+                exp_then_cast: bool = False) -> torch.Tensor:
+    """FP8 attention with ExpCast-FP8 (or exp-then-cast P) and the online mean restore (Eq. 1, 6, 7)."""
     B, H, N, d = _bhnd(Q, "Q")
     T = N // 128 if N % 128 == 0 else 0
     _need(Kq, "Kq", torch.uint8, (B, H, N, d))
@@ -173,7 +175,7 @@ def vc_attn_fwd(Q: torch.Tensor, Kq: torch.Tensor, sK: torch.Tensor, Rq: torch.T
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=Q.device)
     else:
         _need(out, "out", torch.bfloat16, (B, H, N, d))
-    flags = VC_ATTN_NO_MEAN if no_mean else 0
+    flags = (VC_ATTN_NO_MEAN if no_mean else 0) | (VC_ATTN_EXP_THEN_CAST if exp_then_cast else 0)
     _check(lib().vc_attn_fwd(_ptr(Q), _ptr(Kq), _ptr(sK), _ptr(Rq), _ptr(mu), _ptr(sV), B, H, N, d,
                              float(softmax_scale), flags, _ptr(out), _stream()), "vc_attn_fwd")
     return out

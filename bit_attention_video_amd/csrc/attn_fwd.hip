@@ -172,7 +172,10 @@ __device__ __forceinline__ v8i rowsum_ones(int word) {
 
 }  // namespace
 
-template <bool NO_MEAN>
+// ETC: P by exp-then-cast (the comparator of Sec. 3.3): the accumulator input is -m instead
+// of 119.65 - m, so the instruction returns y = a s - m, and P = E4M3_RNE(2^(y/8 + 8)) with
+// v_exp_f32 and the hardware FP8 conversion (y <= 0, so P <= 256 needs no saturation).
+template <bool NO_MEAN, bool ETC>
 __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q,
                                                   const uint8_t* __restrict__ Kq,
                                                   const float* __restrict__ sK,
@@ -432,7 +435,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       for (int i = 0; i < 16; ++i) tm = fmaxf(tm, s[kb][i]);
     tm = pair_max(tm);
     const bool first = j == 0;
-    const float delta = first ? tm - EC_C : fmaxf(tm - EC_C, 0.0f);
+    constexpr float C0 = ETC ? 0.0f : EC_C;
+    const float delta = first ? tm - C0 : fmaxf(tm - C0, 0.0f);
     if (first || __ballot(delta > 0.0f) != 0ull) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -458,10 +462,19 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       for (int wd = 0; wd < 8; ++wd) {
         const int kb = 2 * p + (wd >> 2), i0 = 4 * (wd & 3);
         uint32_t word = 0;
-        word = expcast_byte(s[kb][i0 + 0], 0, word);
-        word = expcast_byte(s[kb][i0 + 1], 1, word);
-        word = expcast_byte(s[kb][i0 + 2], 2, word);
-        word = expcast_byte(s[kb][i0 + 3], 3, word);
+        if constexpr (ETC) {
+          float e[4];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) e[x] = __builtin_amdgcn_exp2f(fmaf(s[kb][i0 + x], 0.125f, 8.0f));
+          int w2 = __builtin_amdgcn_cvt_pk_fp8_f32(e[0], e[1], 0, false);
+          w2 = __builtin_amdgcn_cvt_pk_fp8_f32(e[2], e[3], w2, true);
+          word = (uint32_t)w2;
+        } else {
+          word = expcast_byte(s[kb][i0 + 0], 0, word);
+          word = expcast_byte(s[kb][i0 + 1], 1, word);
+          word = expcast_byte(s[kb][i0 + 2], 2, word);
+          word = expcast_byte(s[kb][i0 + 3], 3, word);
+        }
         pw[p][wd] = (int)word;
       }
     keep(pw[0]);
@@ -559,11 +572,13 @@ hipError_t vc_launch_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float*
                               hipStream_t s) {
   const int nqb = N / 128, nwb = (nqb + 1) / 2;
   const uint32_t G = (uint32_t)BH * (uint32_t)nwb;
-  if (flags & VC_ATTN_NO_MEAN)
-    hipLaunchKernelGGL(k_attn_fwd<true>, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb,
-                       G, L, O);
-  else
-    hipLaunchKernelGGL(k_attn_fwd<false>, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb,
-                       G, L, O);
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb, G, L, O);
+  };
+  const bool no_mean = flags & VC_ATTN_NO_MEAN, etc = flags & VC_ATTN_EXP_THEN_CAST;
+  if (no_mean && etc) launch(k_attn_fwd<true, true>);
+  else if (no_mean) launch(k_attn_fwd<true, false>);
+  else if (etc) launch(k_attn_fwd<false, true>);
+  else launch(k_attn_fwd<false, false>);
   return hipGetLastError();
 }

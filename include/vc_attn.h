@@ -55,6 +55,8 @@ enum vc_status {
 
 /* vc_attn_fwd flags */
 #define VC_ATTN_NO_MEAN 0x1u     /* drop the r * mu term of Eq. 6 (the plain low-bit kernel) */
+#define VC_ATTN_EXP_THEN_CAST 0x2u  /* P by exp2 then an E4M3 cast instead of ExpCast (Sec. 3.3's
+                                       "exp-then-cast" comparator, Table 4's naive FP8) */
 /* vc_vsmooth_demean_quant flags */
 #define VC_DQ_NO_DEMEAN 0x1u     /* mu = 0: quantise V' itself (unsmoothed per-channel baseline) */
 
@@ -96,8 +98,9 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
  * Smoothing and quantisation of K and V in permuted order (Sec. 3.2 Eq. 3-4; App. B).
  *
  * K path: kbar = float32(sum_t K[t] / N) (key channel mean, sum exact in float64);
- *   K' = K[pi] - kbar (float32); per 128-row block j: sK[j] = amax|K'_j| / 448 (1 if 0);
- *   Kq = E4M3_RNE(K' / sK[j]) in [B,H,N,d], rows in permuted order.
+ *   K' = K[pi] - kbar (float32); per 128-row block j: sK[j] = 2^E, the smallest power of two
+ *   with amax|K'_j| <= 448 sK[j] (1 if 0, E >= -100); Kq = E4M3_RNE(K' / sK[j]) in
+ *   [B,H,N,d], rows in permuted order (the division by a power of two is exact).
  * V path: V' = V[pi]; mu_j = float32(sum of the 128 rows of block j / 128);
  *   R = V' - mu_j (float32); sV[c] = amax_t |R[t,c]| / 448 over all N rows (1 if 0);
  *   Rq = E4M3_RNE(R / sV[c]); mu_out[j][c] = bf16_RNE(mu_j[c] / sV[c]).
@@ -131,18 +134,24 @@ int vc_vsmooth_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t*
  *
  * Per (b,h) and query row i (original order; Q is never permuted), over key tiles
  * j = 0 .. N/128-1 of the permuted keys:
- *   Q block of 128 rows: sQ = amax/448 (1 if 0), Qq = E4M3_RNE(Q / sQ)
- *   s = Qq . Kq_j (FP8 matrix instruction, float32 accumulate)
- *   a = float32(float32(L * sQ) * sK[j]),  L = float32(8 log2(e) softmax_scale)
- *   m' = max(m, a * max_k s);  b = float32(119.65 - m')
- *   code = clip(RNE(fma(a, s, b)), 0, 120)  -- the E4M3 byte of P, 2^8 = row maximum
+ *   L = float32(8 log2(e) softmax_scale);  per Q block of 128 rows: X = float32(Q L),
+ *   sQ = 2^E the smallest power of two with amax|X| <= 448 sQ (1 if 0, E >= -100),
+ *   Qq = E4M3_RNE(X / sQ)
+ *   s = Qq . Kq_j (FP8 matrix instruction, float32 accumulate);  a = sQ sK[j] (exact)
+ *   m' = max(m, a max_k s);  b = float32(119.65 - m')
+ *   code = clip(RNE(a s + b), 0, 120)  -- the E4M3 byte of P, 2^8 = row maximum
+ *     (VC_ATTN_EXP_THEN_CAST: code = E4M3_RNE(2^((a s - m')/8 + 8)))
  *   r = sum of decoded codes;  alpha = 2^((m - m')/8)
  *   A = alpha A + P Rq_j + r mu_j;  l = alpha l + r     (mu term dropped by VC_ATTN_NO_MEAN)
  *   O = bf16_RNE(sV * A / l)
+ * a s + b is the accumulator of the scaled FP8 matrix instruction seeded with b (one float32
+ * result per element), so it matches the float32 FMA of the formula up to the instruction's
+ * internal summation order.
  *
  *   Q        in   bf16 [B,H,N,d]
  *   Kq, sK, Rq, mu, sV   in   as written by vc_vsmooth_demean_quant
- *   softmax_scale        0 means 1/sqrt(d)
+ *   softmax_scale        0 means 1/sqrt(d); must be finite and >= 0 (else VC_ERR_SHAPE)
+ *   flags    VC_ATTN_NO_MEAN | VC_ATTN_EXP_THEN_CAST (others: VC_ERR_FLAGS)
  *   O        out  bf16 [B,H,N,d]
  * -------------------------------------------------------------------------------------- */
 int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uint8_t* Rq,

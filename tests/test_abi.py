@@ -54,7 +54,10 @@ def test_attn_fwd_argument_errors():
     assert f(*P, 1, 1, 128, 128, 0.0, 0, None, None) == S["VC_ERR_NULL"]
     # mu may be NULL only with VC_ATTN_NO_MEAN
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 128, 128, 0.0, 0, FAKE, None) == S["VC_ERR_NULL"]
-    assert f(*P, 1, 1, 128, 128, 0.0, 0x2, FAKE, None) == S["VC_ERR_FLAGS"]
+    assert f(*P, 1, 1, 128, 128, 0.0, 0x4, FAKE, None) == S["VC_ERR_FLAGS"]
+    # VC_ATTN_EXP_THEN_CAST (0x2) and both flags pass the flag check (the bad scale is caught next)
+    assert f(*P, 1, 1, 128, 128, -1.0, vc.VC_ATTN_EXP_THEN_CAST, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 128, 128, -1.0, 0x3, FAKE, None) == S["VC_ERR_SHAPE"]
     assert f(*P, 1, 1, 128, 128, -1.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]
     assert f(*P, 1, 1, 128, 128, float("nan"), 0, FAKE, None) == S["VC_ERR_SHAPE"]
     # empty problems are a no-op

@@ -62,6 +62,24 @@ def test_attn_fwd_on_oracle_operands(name, heads, nrows):
         assert err < TOL
 
 
+@pytest.mark.parametrize("no_mean", [False, True])
+def test_attn_fwd_exp_then_cast_mode(no_mean):
+    """VC_ATTN_EXP_THEN_CAST against the oracle's exp-then-cast recurrence (same operands)."""
+    cfg, Q, K, V = config_inputs("medium", [1])
+    N = cfg.N
+    perm = np.random.default_rng(7).permutation(N)
+    ops = [_oracle_ops(values(Q[0, 0]), values(K[0, 0]), values(V[0, 0]), perm)]
+    Kq, sK, Rq, mu, sV = _dev_ops(ops)
+    O = vc.vc_attn_fwd(bf16_dev(Q), Kq, sK, Rq, None if no_mean else mu, sV, no_mean=no_mean,
+                       exp_then_cast=True)
+    O = values(bf16_host_bits(O))
+    rows = rows_sample(N, 512)
+    ref = _emulated(values(Q[0, 0]), ops[0], rows, p_mode="exp_cast", mean=not no_mean)
+    err = T.rel_l2(O[0, 0][rows], ref)
+    note(f"  exp-then-cast no_mean={no_mean}: rel-L2 vs emulated = {err:.3e}")
+    assert err < TOL
+
+
 def test_attn_fwd_no_mean_flag():
     cfg, Q, K, V = config_inputs("medium", [3])
     N = cfg.N
