@@ -45,12 +45,16 @@ __global__ __launch_bounds__(256) void k_kstat_partial(const uint16_t* __restric
   const int q4 = t & 31, rg = t >> 5;
   double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
   const int r0 = ch * VC_KSTAT_CHUNK;
-  for (int i = rg; i < VC_KSTAT_CHUNK; i += 8) {
-    const int r = r0 + i;
-    if (r >= N) break;
-    float v[4];
-    load4(K + ((size_t)bh * N + r) * VC_D + 4 * q4, v);
-    a0 += v[0]; a1 += v[1]; a2 += v[2]; a3 += v[3];
+  // 64 rows per step, 8 loads in flight per thread; N is a multiple of 64, so a step that
+  // starts inside the matrix ends inside it.
+  for (int g = 0; g < VC_KSTAT_CHUNK / 64; ++g) {
+    const int rb = r0 + 64 * g + rg;
+    if (rb >= N) break;
+    float v[8][4];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) load4(K + ((size_t)bh * N + rb + 8 * m) * VC_D + 4 * q4, v[m]);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) { a0 += v[m][0]; a1 += v[m][1]; a2 += v[m][2]; a3 += v[m][3]; }
   }
   part[rg][4 * q4 + 0] = a0;
   part[rg][4 * q4 + 1] = a1;
@@ -170,6 +174,8 @@ __device__ __forceinline__ int pv_slot_of_key(int r) {
   return 64 * p + 32 * g + 16 * ih + 4 * b8 + i4;
 }
 
+constexpr int TILE_ROW = 132;   // LDS bytes per channel row of the transposed tile (128 + pad)
+
 __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                 int N, const float* __restrict__ mu,
                                                 const uint32_t* __restrict__ amax,
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, 
                                                 float* __restrict__ sV) {
   __shared__ float sc[VC_D];
   __shared__ float mus[VC_D];
-  __shared__ __attribute__((aligned(16))) uint8_t tile[VC_D * VC_BLK];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[VC_D * TILE_ROW];
   const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
   const int q4 = t & 31, rg = t >> 5;
   const int nt = N / VC_BLK;
@@ -193,23 +199,35 @@ __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, 
   __syncthreads();
   const float4 s4 = *(const float4*)(sc + 4 * q4);
   const float4 m4 = *(const float4*)(mus + 4 * q4);
+  // Thread (q4, rg) takes the 4-row groups rg, rg+8, rg+16, rg+24 of the tile and channels
+  // 4 q4 .. 4 q4 + 3.  The rows 4 G .. 4 G + 3 of a group land in 4 consecutive PV slots, so
+  // each channel's four codes form one 32-bit word of the transposed tile.
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = rg + 8 * i;
-    const int tok = dq_token(perm, bh, N, j * VC_BLK + r);
-    float v[4];
-    load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
-    const uint32_t w = e4m3x4((v[0] - m4.x) / s4.x, (v[1] - m4.y) / s4.y,
-                              (v[2] - m4.z) / s4.z, (v[3] - m4.w) / s4.w);
-    const int slot = pv_slot_of_key(r);
+  for (int k = 0; k < 4; ++k) {
+    const int r0 = 4 * (rg + 8 * k);
+    uint32_t wc[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tile[(4 * q4 + e) * VC_BLK + slot] = (uint8_t)(w >> (8 * e));
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int tok = dq_token(perm, bh, N, j * VC_BLK + r0 + i4);
+      float v[4];
+      load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
+      const uint32_t w = e4m3x4((v[0] - m4.x) / s4.x, (v[1] - m4.y) / s4.y,
+                                (v[2] - m4.z) / s4.z, (v[3] - m4.w) / s4.w);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wc[e] |= ((w >> (8 * e)) & 0xFFu) << (8 * i4);
+    }
+    const int slot0 = pv_slot_of_key(r0);   // a multiple of 4
+#pragma unroll
+    for (int e = 0; e < 4; ++e) *(uint32_t*)(tile + (4 * q4 + e) * TILE_ROW + slot0) = wc[e];
   }
   __syncthreads();
-  uint4* dst = (uint4*)(Rq + ((size_t)bh * nt + j) * (VC_D * VC_BLK));
-  const uint4* src = (const uint4*)tile;
+  // copy the 128 x 128 bytes out, one 32-bit word per lane (consecutive lanes, consecutive words)
+  uint32_t* dst = (uint32_t*)(Rq + ((size_t)bh * nt + j) * (VC_D * VC_BLK));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[t + 256 * i] = src[t + 256 * i];
+  for (int i = 0; i < 16; ++i) {
+    const int wi = t + 256 * i, c = wi >> 5, x = wi & 31;
+    dst[wi] = *(const uint32_t*)(tile + c * TILE_ROW + 4 * x);
+  }
 }
 
 hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t* perm,
