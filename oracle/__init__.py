@@ -18,6 +18,7 @@ Modules
   analysis  closed forms of App. C/D (Mitchell error, ratio bounds, TV bound)
   vsmooth   k-means grouping, stable label sort, K smoothing and V block
             demeaning with E4M3 quantisation (Sec. 3.2, Eq. 3-5; App. B)
+  rotation  the QK Hadamard rotation fused into the Q/K quantisers (Sec. 4.1, App. B)
   attention exact softmax attention and the emulated tiled VC attention
             (Sec. 3.1 Eq. 1, Sec. 3.2 Eq. 6, Sec. 3.3 Eq. 7)
 
@@ -26,4 +27,4 @@ no printed worked example on the pages; it is pinned by its reductions (exact
 arithmetic -> exact attention; ExpCast row bound of Prop. 3.1; mean-restore
 identity), not by printed values.
 """
-from . import formats, expcast, analysis, vsmooth, attention  # noqa: F401
+from . import formats, expcast, analysis, rotation, vsmooth, attention  # noqa: F401

@@ -147,19 +147,23 @@ def attention_tiled(Qv, sQ, Kv, sK, Rv, mu_t, sV, scale: Optional[float] = None,
 
 
 def vc_attention_emulated(Q, K, V, perm, scale=None, p_mode="expcast", rows=None,
-                          demean: bool = True, k_smooth: bool = True, round_output: bool = True):
+                          demean: bool = True, k_smooth: bool = True, round_output: bool = True,
+                          hadamard: bool = False):
     """Whole emulated VC path for one (batch, head) from bf16 values Q, K, V (N, d) and pi.
 
     Quantises with the oracle's own quantisers (vsmooth), then runs attention_tiled.
     demean=False, perm = identity is the unsmoothed sequence-order FP8 baseline.
+    hadamard=True rotates Q by H and the centred K by H / d before their quantisers (App. B).
     Returns (O, operands dict).
     """
     from . import vsmooth
     N = Q.shape[0]
     perm = np.arange(N) if perm is None else np.asarray(perm)
-    qc, sQ = vsmooth.quantize_q(Q, scale)
+    qc, sQ = vsmooth.quantize_q(Q, scale, hadamard=hadamard)
     if k_smooth:
-        kc, sK = vsmooth.quantize_k(K, perm)
+        kc, sK = vsmooth.quantize_k(K, perm, hadamard=hadamard)
+    elif hadamard:
+        raise ValueError("the rotation is defined on the centred keys")
     else:
         kc, sK = vsmooth.quantize_rows_per_block(fl32(np.asarray(K, dtype=np.float64)[perm]))
     vq = vsmooth.quantize_v(V, perm, demean=demean)

@@ -39,6 +39,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
+from . import rotation
 from .formats import E4M3_MAX, e4m3_encode, fl32, bf16_round
 
 BV = 128  # hardware value block (Sec. 3.2, Eq. 4)
@@ -155,15 +156,22 @@ def key_channel_mean(K) -> np.ndarray:
     return fl32(K.sum(0) / K.shape[0])
 
 
-def quantize_k(K, perm) -> Tuple[np.ndarray, np.ndarray]:
+def quantize_k(K, perm, hadamard: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """K path of App. B: centering stats, gather by pi, mean subtraction, per-block E4M3.
+
+    hadamard=True adds App. B's rotation: the centred rows are rotated by H (rotation.rotate)
+    and quantised per block; the scale then carries the 1/d of H^-T = H / d, so
+    codes * s_K = (K[pi] - kbar) H / d up to the E4M3 rounding.
 
     Returns (codes (N, d) uint8 in permuted order, s_K (N/128,) float32).
     """
     kbar = key_channel_mean(K)
     Kp = fl32(np.asarray(K, dtype=np.float64)[perm])
     Ks = (Kp - kbar[None, :]).astype(np.float32)              # one float32 subtraction
-    return quantize_rows_per_block(Ks)
+    if not hadamard:
+        return quantize_rows_per_block(Ks)
+    codes, s = quantize_rows_per_block(rotation.rotate(Ks))
+    return codes, (s / np.float32(Ks.shape[1])).astype(np.float32)   # exact: d is a power of two
 
 
 def log2e_scale(softmax_scale: float, d: int = 128) -> np.float32:
@@ -173,11 +181,15 @@ def log2e_scale(softmax_scale: float, d: int = 128) -> np.float32:
     return np.float32(8.0 * np.log2(np.e) * softmax_scale)
 
 
-def quantize_q(Q, softmax_scale=None) -> Tuple[np.ndarray, np.ndarray]:
-    """Q path: fl32(Q * L), then per 128-row block E4M3 (Q keeps its token order, Eq. 3)."""
+def quantize_q(Q, softmax_scale=None, hadamard: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Q path: fl32(Q * L), then per 128-row block E4M3 (Q keeps its token order, Eq. 3).
+
+    hadamard=True rotates fl32(Q * L) by H (rotation.rotate) before the quantiser (App. B).
+    """
     Q = np.asarray(Q, dtype=np.float64)
     L = log2e_scale(softmax_scale, Q.shape[1])
-    return quantize_rows_per_block((fl32(Q) * L).astype(np.float32))
+    X = (fl32(Q) * L).astype(np.float32)
+    return quantize_rows_per_block(rotation.rotate(X) if hadamard else X)
 
 
 def block_means(Vp) -> np.ndarray:
