@@ -244,6 +244,28 @@ def main():
     t_etc = time_attn(3, exp_then_cast=True)
     log(f"attention with exp-then-cast P: {t_etc:.2f} ms (ExpCast {t_attn:.2f} ms)")
 
+    # the fused QK Hadamard rotation (App. B): rotated key codes, then attention rotating Q
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ops_rot = vc.vc_vsmooth_demean_quant(Kd, Vd, g["perm"], hadamard=True)
+    e0.record()
+    for _ in range(3):
+        ops_rot = vc.vc_vsmooth_demean_quant(Kd, Vd, g["perm"], hadamard=True)
+    e1.record()
+    torch.cuda.synchronize()
+    t_dq_rot = e0.elapsed_time(e1) / 3
+    vc.vc_attn_fwd(Qd, ops_rot["Kq"], ops_rot["sK"], ops_rot["Rq"], ops_rot["mu"], ops_rot["sV"], out=O,
+                   hadamard=True)
+    e0.record()
+    for _ in range(3):
+        vc.vc_attn_fwd(Qd, ops_rot["Kq"], ops_rot["sK"], ops_rot["Rq"], ops_rot["mu"], ops_rot["sV"], out=O,
+                       hadamard=True)
+    e1.record()
+    torch.cuda.synchronize()
+    t_attn_rot = e0.elapsed_time(e1) / 3
+    assert torch.isfinite(O.float()).all(), "non-finite attention output (rotated)"
+    del ops_rot
+    log(f"QK rotation: demean_quant {t_dq_rot:.3f} ms, attention {t_attn_rot:.2f} ms")
+
     if args.attn_only_iters:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -287,6 +309,9 @@ def main():
         "vsmooth_over_attn": {k2: round(v2, 4) for k2, v2 in amort.items()},
         "p_path": {"expcast_ms": round(t_attn, 4), "exp_then_cast_ms": round(t_etc, 4),
                    "expcast_speedup": round(t_etc / t_attn, 4)},
+        "qk_rotation": {"demean_quant_ms": round(t_dq_rot, 4), "attn_ms": round(t_attn_rot, 4),
+                        "attn_over_unrotated": round(t_attn_rot / t_attn, 4),
+                        "demean_quant_over_unrotated": round(t_dq_rot / t_dq, 4)},
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")

@@ -25,13 +25,16 @@ import torch
 __all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_attn_fwd",
            "vc_attention", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
            "vc_test_label_sort", "rq_tiled_to_natural", "rq_natural_to_tiled", "LIB_PATH",
-           "VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_DQ_NO_DEMEAN", "STATUS"]
+           "VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_ATTN_HADAMARD", "VC_DQ_NO_DEMEAN",
+           "VC_DQ_HADAMARD", "STATUS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvcattn.so")
 
 VC_ATTN_NO_MEAN = 0x1
 VC_ATTN_EXP_THEN_CAST = 0x2
+VC_ATTN_HADAMARD = 0x4
 VC_DQ_NO_DEMEAN = 0x1
+VC_DQ_HADAMARD = 0x2
 STATUS = {"VC_OK": 0, "VC_ERR_NULL": -1, "VC_ERR_SHAPE": -2, "VC_ERR_K": -3, "VC_ERR_ITERS": -4,
           "VC_ERR_WORKSPACE": -5, "VC_ERR_OVERFLOW": -6, "VC_ERR_FLAGS": -7, "VC_ERR_HIP": -8}
 
@@ -136,8 +139,10 @@ def vc_vsmooth_group(V: torch.Tensor, k: int, iters: int, C_init: Optional[torch
 
 
 def vc_vsmooth_demean_quant(K: torch.Tensor, V: torch.Tensor, perm: Optional[torch.Tensor] = None,
-                            no_demean: bool = False):
-    """E4M3 operands of the VC path from bf16 K, V and pi (Sec. 3.2, Eq. 4; App. B)."""
+                            no_demean: bool = False, hadamard: bool = False):
+    """E4M3 operands of the VC path from bf16 K, V and pi (Sec. 3.2, Eq. 4; App. B).
+
+    hadamard=True quantises the rotated keys (K[pi] - kbar) H with the scale divided by 128."""
     B, H, N, d = _bhnd(K, "K")
     _need(V, "V", torch.bfloat16, (B, H, N, d))
     if perm is not None:
@@ -151,7 +156,7 @@ def vc_vsmooth_demean_quant(K: torch.Tensor, V: torch.Tensor, perm: Optional[tor
     sV = torch.empty((B, H, d), dtype=torch.float32, device=dev)
     nws = lib().vc_demean_quant_workspace_size(B, H, N)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
-    flags = VC_DQ_NO_DEMEAN if no_demean else 0
+    flags = (VC_DQ_NO_DEMEAN if no_demean else 0) | (VC_DQ_HADAMARD if hadamard else 0)
     _check(lib().vc_vsmooth_demean_quant(_ptr(K), _ptr(V), _ptr(perm), B, H, N, d, flags, _ptr(Kq), _ptr(sK),
                                          _ptr(Rq), _ptr(mu), _ptr(sV), _ptr(ws), nws, _stream()),
            "vc_vsmooth_demean_quant")
@@ -161,8 +166,11 @@ def vc_vsmooth_demean_quant(K: torch.Tensor, V: torch.Tensor, perm: Optional[tor
 def vc_attn_fwd(Q: torch.Tensor, Kq: torch.Tensor, sK: torch.Tensor, Rq: torch.Tensor,
                 mu: Optional[torch.Tensor], sV: torch.Tensor, softmax_scale: float = 0.0,
                 no_mean: bool = False, out: Optional[torch.Tensor] = None,
-                exp_then_cast: bool = False) -> torch.Tensor:
-    """FP8 attention with ExpCast-FP8 (or exp-then-cast P) and the online mean restore (Eq. 1, 6, 7)."""
+                exp_then_cast: bool = False, hadamard: bool = False) -> torch.Tensor:
+    """FP8 attention with ExpCast-FP8 (or exp-then-cast P) and the online mean restore (Eq. 1, 6, 7).
+
+    hadamard=True rotates the queries by H before quantising them; the keys must then come from
+    vc_vsmooth_demean_quant(..., hadamard=True)."""
     B, H, N, d = _bhnd(Q, "Q")
     T = N // 128 if N % 128 == 0 else 0
     _need(Kq, "Kq", torch.uint8, (B, H, N, d))
@@ -175,17 +183,19 @@ def vc_attn_fwd(Q: torch.Tensor, Kq: torch.Tensor, sK: torch.Tensor, Rq: torch.T
         out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=Q.device)
     else:
         _need(out, "out", torch.bfloat16, (B, H, N, d))
-    flags = (VC_ATTN_NO_MEAN if no_mean else 0) | (VC_ATTN_EXP_THEN_CAST if exp_then_cast else 0)
+    flags = ((VC_ATTN_NO_MEAN if no_mean else 0) | (VC_ATTN_EXP_THEN_CAST if exp_then_cast else 0)
+             | (VC_ATTN_HADAMARD if hadamard else 0))
     _check(lib().vc_attn_fwd(_ptr(Q), _ptr(Kq), _ptr(sK), _ptr(Rq), _ptr(mu), _ptr(sV), B, H, N, d,
                              float(softmax_scale), flags, _ptr(out), _stream()), "vc_attn_fwd")
     return out
 
 
-def vc_attention(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool = False):
+def vc_attention(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool = False,
+                 hadamard: bool = False):
     """demean_quant then attn_fwd: O = attention(Q, K, V) on the VC path for a given pi."""
-    ops = vc_vsmooth_demean_quant(K, V, perm, no_demean=no_demean)
+    ops = vc_vsmooth_demean_quant(K, V, perm, no_demean=no_demean, hadamard=hadamard)
     return vc_attn_fwd(Q, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"], softmax_scale,
-                       no_mean=no_demean)
+                       no_mean=no_demean, hadamard=hadamard)
 
 
 def vc_test_expcast(u: torch.Tensor) -> torch.Tensor:

@@ -140,7 +140,7 @@ int vc_vsmooth_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t*
   if (st < 0) return st;
   if (st == 1) return VC_OK;
   if (!K || !V || !Kq || !sK || !Rq || !mu_out || !sV || !ws) return VC_ERR_NULL;
-  if (flags & ~VC_DQ_NO_DEMEAN) return VC_ERR_FLAGS;
+  if (flags & ~(VC_DQ_NO_DEMEAN | VC_DQ_HADAMARD)) return VC_ERR_FLAGS;
   int BH = B * H;
   vc_dq_ws L = vc_dq_ws_layout(BH, N);
   if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
@@ -156,7 +156,7 @@ int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uin
   if (st == 1) return VC_OK;
   if (!Q || !Kq || !sK || !Rq || !sV || !O) return VC_ERR_NULL;
   if (!mu && !(flags & VC_ATTN_NO_MEAN)) return VC_ERR_NULL;
-  if (flags & ~(VC_ATTN_NO_MEAN | VC_ATTN_EXP_THEN_CAST)) return VC_ERR_FLAGS;
+  if (flags & ~(VC_ATTN_NO_MEAN | VC_ATTN_EXP_THEN_CAST | VC_ATTN_HADAMARD)) return VC_ERR_FLAGS;
   if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return VC_ERR_SHAPE;
   // L = float32(8 log2(e) * scale), the scale taken in double (1/sqrt(d) when 0 is passed)
   const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;

@@ -46,6 +46,10 @@
 // when the maximum grows), and once per group A += mu~^T rho with the bf16 32x32x16
 // instruction (mu~ is exact bf16; rho is split into bf16 hi + lo, 16 significant bits).
 // Epilogue: O = bf16(A * sV / l) (App. B: one multiply by sV serves both terms).
+//
+// QK rotation (App. B's Q pass; the fused QK Hadamard of Sec. 4.1): with VC_ATTN_HADAMARD the
+// prologue rotates each query row Q L by the Sylvester Hadamard matrix H before taking sQ and
+// the codes; the key codes then come from vc_vsmooth_demean_quant's matching K H / 128.
 #include "vc_common.h"
 #include "vc_internal.h"
 #include "vc_attn.h"
@@ -175,7 +179,32 @@ __device__ __forceinline__ v8i rowsum_ones(int word) {
 // ETC: P by exp-then-cast (the comparator of Sec. 3.3): the accumulator input is -m instead
 // of 119.65 - m, so the instruction returns y = a s - m, and P = E4M3_RNE(2^(y/8 + 8)) with
 // v_exp_f32 and the hardware FP8 conversion (y <= 0, so P <= 256 needs no saturation).
-template <bool NO_MEAN, bool ETC>
+// Rotation of one query row by the Sylvester Hadamard matrix H (entries +-1, App. B's Q pass).
+// Lane (q, hl) holds channels 64 c + 32 hl + 8 m + j of row q as x[32 c + 8 m + j]: local index
+// bits 0-4 are channel bits 0-4, local bit 5 is channel bit 6, and channel bit 5 is the lane
+// half.  The butterflies run in float64, where the signed sum of the 128 float32 terms is exact
+// whatever the order, and each result is rounded to float32 once.
+__device__ __forceinline__ void hadamard_q_row(float* x, int hl) {
+  double y[64];
+#pragma unroll
+  for (int k = 0; k < 64; ++k) y[k] = (double)x[k];
+#pragma unroll
+  for (int b = 1; b < 64; b <<= 1)
+#pragma unroll
+    for (int k = 0; k < 64; ++k)
+      if (!(k & b)) {
+        const double u = y[k], v = y[k | b];
+        y[k] = u + v;
+        y[k | b] = u - v;
+      }
+#pragma unroll
+  for (int k = 0; k < 64; ++k) {
+    const double o = __shfl_xor(y[k], 32, 64);
+    x[k] = (float)(hl ? o - y[k] : y[k] + o);
+  }
+}
+
+template <bool NO_MEAN, bool ETC, bool HAD>
 __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q,
                                                   const uint8_t* __restrict__ Kq,
                                                   const float* __restrict__ sK,
@@ -248,10 +277,10 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     mean_row(clampT(i));
   }
 
-  // ---- prologue: Q L, its block scale sQ = 2^E (amax over the 128 x 128 block), E4M3 ----
+  // ---- prologue: Q L (rotated by H when HAD), its block scale sQ = 2^E (amax over the
+  // 128 x 128 block), E4M3 ----
   const uint16_t* qrow = Q + (headN + qi) * VC_D;
   float qs[64];
-  float amax = 0.0f;
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -260,12 +289,14 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_to_f32(wd[e] & 0xFFFFu) * L, hi = bf16_to_f32(wd[e] >> 16) * L;
-        qs[32 * c + 8 * m + 2 * e] = lo;
-        qs[32 * c + 8 * m + 2 * e + 1] = hi;
-        amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+        qs[32 * c + 8 * m + 2 * e] = bf16_to_f32(wd[e] & 0xFFFFu) * L;
+        qs[32 * c + 8 * m + 2 * e + 1] = bf16_to_f32(wd[e] >> 16) * L;
       }
     }
+  if constexpr (HAD) hadamard_q_row(qs, hl);
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 64; ++k) amax = fmaxf(amax, fabsf(qs[k]));
   amax = wave_max(amax);
   if (lane == 0) red[w] = amax;
   __syncthreads();   // red[] and the cleared ring
@@ -576,9 +607,16 @@ hipError_t vc_launch_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float*
     hipLaunchKernelGGL(kern, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb, G, L, O);
   };
   const bool no_mean = flags & VC_ATTN_NO_MEAN, etc = flags & VC_ATTN_EXP_THEN_CAST;
-  if (no_mean && etc) launch(k_attn_fwd<true, true>);
-  else if (no_mean) launch(k_attn_fwd<true, false>);
-  else if (etc) launch(k_attn_fwd<false, true>);
-  else launch(k_attn_fwd<false, false>);
+  if (flags & VC_ATTN_HADAMARD) {
+    if (no_mean && etc) launch(k_attn_fwd<true, true, true>);
+    else if (no_mean) launch(k_attn_fwd<true, false, true>);
+    else if (etc) launch(k_attn_fwd<false, true, true>);
+    else launch(k_attn_fwd<false, false, true>);
+  } else {
+    if (no_mean && etc) launch(k_attn_fwd<true, true, false>);
+    else if (no_mean) launch(k_attn_fwd<true, false, false>);
+    else if (etc) launch(k_attn_fwd<false, true, false>);
+    else launch(k_attn_fwd<false, false, false>);
+  }
   return hipGetLastError();
 }

@@ -10,7 +10,8 @@
 //   k_kstat_partial  float64 channel sums of K per 1024-row chunk
 //   k_kstat_final    kbar = float32(sum / N) in chunk order
 //   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = 2^E (smallest power of two
-//                    with amax <= 448 sK, an E8M0 block scale), codes
+//                    with amax <= 448 sK, an E8M0 block scale), codes; with VC_DQ_HADAMARD the
+//                    rows K' H (Sylvester H, App. B) are quantised and sK = 2^(E-7)
 //   k_vclear         zero the per-channel |R| maxima
 //   k_vpass1         per block of V[pi]: mu_j (float64 sum / 128), |R| maxima -> atomicMax
 //   k_vpass2         sV = amax/448; codes of R / sV into the tile-transposed PV operand order;
@@ -77,7 +78,36 @@ __global__ __launch_bounds__(128) void k_kstat_final(const double* __restrict__ 
   kbar[(size_t)bh * VC_D + t] = (float)(s / (double)N);
 }
 
-__global__ __launch_bounds__(256) void k_kquant(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
+// Rotation of one centred key row by the Sylvester Hadamard matrix H (entries +-1; App. B's K
+// pass).  The 32 lanes of a half-wave hold the row, lane q4 the channels 4 q4 .. 4 q4 + 3: channel
+// bits 0-1 are local, bits 2-6 are the bits of q4.  The butterflies run in float64, where the
+// signed sum of the 128 float32 terms is exact whatever the order, and round to float32 once.
+__device__ __forceinline__ void hadamard_k_row(float* x, int q4) {
+  double a0 = x[0], a1 = x[1], a2 = x[2], a3 = x[3];
+  const double b0 = a0 + a1, b1 = a0 - a1, b2 = a2 + a3, b3 = a2 - a3;
+  a0 = b0 + b2;
+  a2 = b0 - b2;
+  a1 = b1 + b3;
+  a3 = b1 - b3;
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) {
+    const bool upper = q4 & m;   // this lane holds the partner with channel bit set
+    const double o0 = __shfl_xor(a0, m, 64), o1 = __shfl_xor(a1, m, 64);
+    const double o2 = __shfl_xor(a2, m, 64), o3 = __shfl_xor(a3, m, 64);
+    a0 = upper ? o0 - a0 : a0 + o0;
+    a1 = upper ? o1 - a1 : a1 + o1;
+    a2 = upper ? o2 - a2 : a2 + o2;
+    a3 = upper ? o3 - a3 : a3 + o3;
+  }
+  x[0] = (float)a0;
+  x[1] = (float)a1;
+  x[2] = (float)a2;
+  x[3] = (float)a3;
+}
+
+// HAD: codes of (K[pi] - kbar) H; the stored scale is 2^(E-7), carrying the 1/128 of H / 128.
+template <bool HAD>
+__global__ __launch_bounds__(256, 4) void k_kquant(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
                                                 const float* __restrict__ kbar, int N,
                                                 uint8_t* __restrict__ Kq, float* __restrict__ sK) {
   __shared__ float red4[4];
@@ -95,13 +125,27 @@ __global__ __launch_bounds__(256) void k_kquant(const uint16_t* __restrict__ K, 
     x[i][1] = v[1] - kb.y;
     x[i][2] = v[2] - kb.z;
     x[i][3] = v[3] - kb.w;
+    if constexpr (!HAD)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+  }
+  if constexpr (HAD) {
+    // two rows at a time: interleaving all rows' exchanges would need 16 live float64 sets
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      hadamard_k_row(x[i], q4);
+      hadamard_k_row(x[i + 1], q4);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
   }
   amax = block_max_256(amax, red4);
   const int E = pow2_block_exponent(amax);
   const float inv = __builtin_ldexpf(1.0f, -E);   // exact: the scale is a power of two
-  const float s = __builtin_ldexpf(1.0f, E);
+  const float s = __builtin_ldexpf(1.0f, HAD ? E - 7 : E);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = j * VC_BLK + rg + 8 * i;
@@ -242,7 +286,10 @@ hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const in
   uint32_t* amax = (uint32_t*)(ws + L.amax);
   hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
-  hipLaunchKernelGGL(k_kquant, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
+  if (flags & VC_DQ_HADAMARD)
+    hipLaunchKernelGGL(k_kquant<true>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
+  else
+    hipLaunchKernelGGL(k_kquant<false>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
   hipLaunchKernelGGL(k_vclear, dim3(BH), dim3(128), 0, s, amax);
   hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(256), 0, s, V, perm, N,
                      (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amax);

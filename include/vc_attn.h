@@ -57,8 +57,11 @@ enum vc_status {
 #define VC_ATTN_NO_MEAN 0x1u     /* drop the r * mu term of Eq. 6 (the plain low-bit kernel) */
 #define VC_ATTN_EXP_THEN_CAST 0x2u  /* P by exp2 then an E4M3 cast instead of ExpCast (Sec. 3.3's
                                        "exp-then-cast" comparator, Table 4's naive FP8) */
+#define VC_ATTN_HADAMARD 0x4u    /* rotate Q L by H before quantising (App. B's Q pass, the fused
+                                    QK Hadamard of Sec. 4.1); pair with VC_DQ_HADAMARD keys */
 /* vc_vsmooth_demean_quant flags */
 #define VC_DQ_NO_DEMEAN 0x1u     /* mu = 0: quantise V' itself (unsmoothed per-channel baseline) */
+#define VC_DQ_HADAMARD 0x2u      /* quantise the rotated keys K' H, scale / 128 (App. B's K pass) */
 
 /* Human-readable name of a vc_status. Never NULL. */
 const char* vc_strerror(int status);
@@ -105,6 +108,13 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
  *   R = V' - mu_j (float32); sV[c] = amax_t |R[t,c]| / 448 over all N rows (1 if 0);
  *   Rq = E4M3_RNE(R / sV[c]); mu_out[j][c] = bf16_RNE(mu_j[c] / sV[c]).
  *   Flag VC_DQ_NO_DEMEAN sets mu = 0 (quantise V' itself).
+ * Flag VC_DQ_HADAMARD (App. B's K pass with the QK rotation; Sec. 4.1 "Baselines"): the
+ *   blocks of Y = float32(K' H) are quantised instead of K', with H the Sylvester Hadamard
+ *   matrix of order 128 (H[r][c] = (-1)^popcount(r & c)); each Y element is the float32
+ *   rounding of the signed sum of 128 float32 terms, taken in float64 (exact unless a row's
+ *   terms span more than about 22 binades).  sK[j] = 2^(E-7) with 2^E the scale of block j
+ *   of Y, so Kq * sK = K' H / 128 = K' H^-T and the scores are those of unrotated keys once
+ *   the queries are rotated by H (vc_attn_fwd's VC_ATTN_HADAMARD).
  * Every division is one correctly rounded float32 division; E4M3 is OCP E4M3FN with
  * round-to-nearest-even (|x| <= 448 by construction).
  *
@@ -134,7 +144,8 @@ int vc_vsmooth_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t*
  *
  * Per (b,h) and query row i (original order; Q is never permuted), over key tiles
  * j = 0 .. N/128-1 of the permuted keys:
- *   L = float32(8 log2(e) softmax_scale);  per Q block of 128 rows: X = float32(Q L),
+ *   L = float32(8 log2(e) softmax_scale);  per Q block of 128 rows: X = float32(Q L)
+ *   (VC_ATTN_HADAMARD: X = float32(float32(Q L) H), H and its rounding as for VC_DQ_HADAMARD),
  *   sQ = 2^E the smallest power of two with amax|X| <= 448 sQ (1 if 0, E >= -100),
  *   Qq = E4M3_RNE(X / sQ)
  *   s = Qq . Kq_j (FP8 matrix instruction, float32 accumulate);  a = sQ sK[j] (exact)
@@ -151,7 +162,9 @@ int vc_vsmooth_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t*
  *   Q        in   bf16 [B,H,N,d]
  *   Kq, sK, Rq, mu, sV   in   as written by vc_vsmooth_demean_quant
  *   softmax_scale        0 means 1/sqrt(d); must be finite and >= 0 (else VC_ERR_SHAPE)
- *   flags    VC_ATTN_NO_MEAN | VC_ATTN_EXP_THEN_CAST (others: VC_ERR_FLAGS)
+ *   flags    VC_ATTN_NO_MEAN | VC_ATTN_EXP_THEN_CAST | VC_ATTN_HADAMARD (others: VC_ERR_FLAGS).
+ *            VC_ATTN_HADAMARD needs keys written with VC_DQ_HADAMARD and the reverse; a mixed
+ *            pair is not detected and gives the scores of a different operator.
  *   O        out  bf16 [B,H,N,d]
  * -------------------------------------------------------------------------------------- */
 int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uint8_t* Rq,

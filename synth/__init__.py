@@ -19,6 +19,9 @@ Recipe (one numpy Generator per (config, head, tensor), seeded by
 * Outliers: round(f * N) tokens drawn without replacement; in each head a set
   of 4 channels is drawn and those channels of every outlier token are
   multiplied by a per-token factor U[20, 50] (or a fixed factor).
+* Q/K channel outliers (the case a QK rotation is for): in each head a set of
+  qk_outlier_channels channels is drawn and those channels of Q and K are
+  multiplied by qk_outlier_scale for every token.
 * Draws are float32, rounded once to bf16 (round to nearest even) by torch.
 
 Tokens n <-> (t, y, x) in row-major order.  When N exceeds T*H*W (the N=70,016
@@ -57,6 +60,8 @@ class Config:
     noise_std: float = 0.3
     steps: int = 1              # permutation-reuse steps
     step_noise_std: float = 0.05
+    qk_outlier_channels: int = 0      # Q/K channels scaled by qk_outlier_scale in every token
+    qk_outlier_scale: float = 1.0
 
 
 CONFIGS: Dict[str, Config] = {
@@ -70,6 +75,9 @@ CONFIGS: Dict[str, Config] = {
                     k_true=128, outlier_frac=0.003, k_bias_var=2.0, steps=4),
     "long": Config("long", 5, 1, 24, 115200, 128, k=256, iters=10, grid=(30, 48, 80), v_kind="field",
                    k_true=256, outlier_frac=0.003, k_bias_var=2.0),
+    "qk_outlier": Config("qk_outlier", 6, 1, 4, 8192, 128, k=64, iters=10, grid=(8, 32, 32), v_kind="field",
+                         k_true=64, outlier_frac=0.003, k_bias_var=2.0, qk_outlier_channels=4,
+                         qk_outlier_scale=25.0),
 }
 
 
@@ -154,6 +162,10 @@ def make_head(cfg: Config, head: int, step: int = 0) -> Tuple[np.ndarray, np.nda
     k = krng.standard_normal((N, d), dtype=np.float32)
     if cfg.k_bias_var > 0:
         k += np.float32(np.sqrt(cfg.k_bias_var)) * krng.standard_normal(d, dtype=np.float32)[None, :]
+    if cfg.qk_outlier_channels > 0:
+        ch = np.random.default_rng([cfg.cfg_id, head, 4]).choice(d, cfg.qk_outlier_channels, replace=False)
+        q[:, ch] *= np.float32(cfg.qk_outlier_scale)
+        k[:, ch] *= np.float32(cfg.qk_outlier_scale)
     v = _v_head(cfg, head, step)
     return bf16_bits(q), bf16_bits(k), bf16_bits(v)
 

@@ -33,6 +33,10 @@ def test_header_statuses_match_binding():
     for name, val in S.items():
         m = re.search(rf"\b{name}\s*=\s*(-?\d+)", text)
         assert m and int(m.group(1)) == val, name
+    for name in ("VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_ATTN_HADAMARD", "VC_DQ_NO_DEMEAN",
+                 "VC_DQ_HADAMARD"):
+        m = re.search(rf"#define\s+{name}\s+(0x[0-9a-fA-F]+)u", text)
+        assert m and int(m.group(1), 16) == getattr(vc, name), name
 
 
 def test_strerror():
@@ -54,10 +58,12 @@ def test_attn_fwd_argument_errors():
     assert f(*P, 1, 1, 128, 128, 0.0, 0, None, None) == S["VC_ERR_NULL"]
     # mu may be NULL only with VC_ATTN_NO_MEAN
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 128, 128, 0.0, 0, FAKE, None) == S["VC_ERR_NULL"]
-    assert f(*P, 1, 1, 128, 128, 0.0, 0x4, FAKE, None) == S["VC_ERR_FLAGS"]
-    # VC_ATTN_EXP_THEN_CAST (0x2) and both flags pass the flag check (the bad scale is caught next)
+    assert f(*P, 1, 1, 128, 128, 0.0, 0x8, FAKE, None) == S["VC_ERR_FLAGS"]
+    # VC_ATTN_EXP_THEN_CAST (0x2), VC_ATTN_HADAMARD (0x4) and all of them together pass the flag
+    # check (the bad scale is caught next)
     assert f(*P, 1, 1, 128, 128, -1.0, vc.VC_ATTN_EXP_THEN_CAST, FAKE, None) == S["VC_ERR_SHAPE"]
-    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 128, 128, -1.0, 0x3, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert f(*P, 1, 1, 128, 128, -1.0, vc.VC_ATTN_HADAMARD, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 1, 1, 128, 128, -1.0, 0x7, FAKE, None) == S["VC_ERR_SHAPE"]
     assert f(*P, 1, 1, 128, 128, -1.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]
     assert f(*P, 1, 1, 128, 128, float("nan"), 0, FAKE, None) == S["VC_ERR_SHAPE"]
     # empty problems are a no-op
@@ -94,6 +100,7 @@ def test_demean_quant_argument_errors():
     assert f(*args(N=129)) == S["VC_ERR_SHAPE"]
     assert f(*args(K=None)) == S["VC_ERR_NULL"]
     assert f(*args(flags=0x4)) == S["VC_ERR_FLAGS"]
+    assert f(*args(flags=0x3, nws=0)) == S["VC_ERR_WORKSPACE"]      # both flags are known
     assert f(*args(nws=0)) == S["VC_ERR_WORKSPACE"]
     assert f(*args(N=0)) == S["VC_OK"]
 
