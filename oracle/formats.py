@@ -1,5 +1,8 @@
 """Number formats used by the method (oracle; test infrastructure only).
 
+E2M1 (the 4-bit element of the MX formats, the analogue of the pages' NVFP4 elements in the
+4-bit path, Sec. 3.2 after Eq. 4 and App. A) is defined at e2m1_decode.
+
 E4M3 is the OCP 8-bit float E4M3FN that the pages' E4M3 refers to: a byte
 with sign s, 4-bit exponent field e and 3-bit mantissa field m stores
 2^(e-7) * (1 + m/8) for e >= 1 (VC-Attention, Sec. 3.3, the decoding rule
@@ -56,6 +59,40 @@ def e4m3_encode(x) -> np.ndarray:
     out = np.where(neg, code | 0x80, code).astype(np.uint8)
     out = np.where(np.isnan(x), np.uint8(0x7F), out)
     return out
+
+
+E2M1_MAX = 6.0
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 (OCP MX FP4) codes (low nibble of uint8) -> float64 values, from the field layout:
+    sign bit 3, exponent field e = bits 2-1 (bias 1), mantissa bit 0; 2^(e-1) (1 + m/2) for
+    e >= 1, m/2 for e = 0.  No infinities or NaNs; the largest magnitude is 6."""
+    c = np.asarray(codes, dtype=np.int64) & 0xF
+    sign = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    val = np.where(e == 0, m / 2.0, np.ldexp(1.0 + m / 2.0, (e - 1).astype(np.int64)))
+    return sign * val
+
+
+_E2M1_POS = e2m1_decode(np.arange(8))       # 0, 0.5, 1, 1.5, 2, 3, 4, 6
+
+
+def e2m1_encode(x) -> np.ndarray:
+    """Values -> E2M1 codes (uint8, 0..15): nearest value, ties to the even code, saturating at
+    +-6; the sign bit is the input's (a negative value that rounds to zero gives 0x8)."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E2M1_MAX)
+    hi = np.minimum(np.searchsorted(_E2M1_POS, a, side="left"), 7)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E2M1_POS[lo]
+    dhi = _E2M1_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == _E2M1_POS[hi], hi, code).astype(np.uint8)
+    return np.where(neg, code | 0x8, code).astype(np.uint8)
 
 
 def fl32(x) -> np.ndarray:
