@@ -23,7 +23,8 @@ import numpy as np
 import torch
 
 __all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_attn_fwd",
-           "vc_attention", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
+           "vc_attention", "vc_vsmooth_demean_quant_mx4", "vc_attn_fwd_mx4", "vc_attention_mx4",
+           "vc_test_fp4_encode", "unpack_fp4", "pack_fp4", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
            "vc_test_label_sort", "rq_tiled_to_natural", "rq_natural_to_tiled", "LIB_PATH",
            "VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_ATTN_HADAMARD", "VC_DQ_NO_DEMEAN",
            "VC_DQ_HADAMARD", "STATUS"]
@@ -52,6 +53,9 @@ _SIGNATURES = {
     "vc_demean_quant_workspace_size": (_Z, [_I, _I, _I]),
     "vc_vsmooth_demean_quant": (_I, [_P, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "vc_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
+    "vc_vsmooth_demean_quant_mx4": (_I, [_P, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "vc_attn_fwd_mx4": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
+    "vc_test_fp4_encode": (_I, [_P, _P, _Z, _P]),
     "vc_test_expcast": (_I, [_P, _P, _Z, _P]),
     "vc_test_e4m3_encode": (_I, [_P, _P, _Z, _P]),
     "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
@@ -198,6 +202,69 @@ def vc_attention(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool
                        no_mean=no_demean, hadamard=hadamard)
 
 
+def vc_vsmooth_demean_quant_mx4(K: torch.Tensor, V: torch.Tensor, perm: Optional[torch.Tensor] = None,
+                                no_demean: bool = False, hadamard: bool = False):
+    """4-bit (MX E2M1, per-32 E8M0 scales) operands of the VC path (Sec. 3.2 Eq. 4; App. B)."""
+    B, H, N, d = _bhnd(K, "K")
+    _need(V, "V", torch.bfloat16, (B, H, N, d))
+    if perm is not None:
+        _need(perm, "perm", torch.int32, (B, H, N))
+    dev = K.device
+    T = N // 128 if N % 128 == 0 else 0
+    Kq4 = torch.empty((B, H, N, d // 2), dtype=torch.uint8, device=dev)
+    sK4 = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=dev)
+    Rq4 = torch.empty((B, H, T, d, 64), dtype=torch.uint8, device=dev)
+    sR4 = torch.empty((B, H, T, d, 4), dtype=torch.uint8, device=dev)
+    mu = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    nws = lib().vc_demean_quant_workspace_size(B, H, N)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    flags = (VC_DQ_NO_DEMEAN if no_demean else 0) | (VC_DQ_HADAMARD if hadamard else 0)
+    _check(lib().vc_vsmooth_demean_quant_mx4(_ptr(K), _ptr(V), _ptr(perm), B, H, N, d, flags, _ptr(Kq4),
+                                             _ptr(sK4), _ptr(Rq4), _ptr(sR4), _ptr(mu), _ptr(ws), nws, _stream()),
+           "vc_vsmooth_demean_quant_mx4")
+    return {"Kq4": Kq4, "sK4": sK4, "Rq4": Rq4, "sR4": sR4, "mu": mu}
+
+
+def vc_attn_fwd_mx4(Q: torch.Tensor, Kq4: torch.Tensor, sK4: torch.Tensor, Rq4: torch.Tensor,
+                    sR4: torch.Tensor, mu: Optional[torch.Tensor], softmax_scale: float = 0.0,
+                    no_mean: bool = False, hadamard: bool = False,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """4-bit attention: MX E2M1 Q, K, P and residual, P = 2^(S L4 - m), mean restore (Eq. 1, 6)."""
+    B, H, N, d = _bhnd(Q, "Q")
+    T = N // 128 if N % 128 == 0 else 0
+    _need(Kq4, "Kq4", torch.uint8, (B, H, N, d // 2))
+    _need(sK4, "sK4", torch.uint8, (B, H, N, d // 32))
+    _need(Rq4, "Rq4", torch.uint8, (B, H, T, d, 64))
+    _need(sR4, "sR4", torch.uint8, (B, H, T, d, 4))
+    if mu is not None or not no_mean:
+        _need(mu, "mu", torch.bfloat16, (B, H, T, d))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=Q.device)
+    else:
+        _need(out, "out", torch.bfloat16, (B, H, N, d))
+    flags = (VC_ATTN_NO_MEAN if no_mean else 0) | (VC_ATTN_HADAMARD if hadamard else 0)
+    _check(lib().vc_attn_fwd_mx4(_ptr(Q), _ptr(Kq4), _ptr(sK4), _ptr(Rq4), _ptr(sR4), _ptr(mu), B, H, N, d,
+                                 float(softmax_scale), flags, _ptr(out), _stream()), "vc_attn_fwd_mx4")
+    return out
+
+
+def vc_attention_mx4(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool = False,
+                     hadamard: bool = False):
+    """4-bit demean_quant then 4-bit attention for a given pi."""
+    ops = vc_vsmooth_demean_quant_mx4(K, V, perm, no_demean=no_demean, hadamard=hadamard)
+    return vc_attn_fwd_mx4(Q, ops["Kq4"], ops["sK4"], ops["Rq4"], ops["sR4"], ops["mu"], softmax_scale,
+                           no_mean=no_demean, hadamard=hadamard)
+
+
+def vc_test_fp4_encode(x: torch.Tensor) -> torch.Tensor:
+    """Byte i = E2M1 codes of (x[2i], x[2i+1]), x[2i] in the low nibble."""
+    _need(x, "x", torch.float32)
+    n = x.numel()
+    codes = torch.empty(n // 2, dtype=torch.uint8, device=x.device)
+    _check(lib().vc_test_fp4_encode(_ptr(x), _ptr(codes), n, _stream()), "vc_test_fp4_encode")
+    return codes
+
+
 def vc_test_expcast(u: torch.Tensor) -> torch.Tensor:
     _need(u, "u", torch.float32)
     codes = torch.empty(u.shape, dtype=torch.uint8, device=u.device)
@@ -266,3 +333,15 @@ def rq_natural_to_tiled(R: torch.Tensor) -> torch.Tensor:
     t = R.reshape(B, H, T, 128, d)
     idx = torch.as_tensor(KEY_OF_SLOT, device=R.device)
     return t.index_select(3, idx).permute(0, 1, 2, 4, 3).contiguous()
+
+
+def unpack_fp4(x: torch.Tensor) -> torch.Tensor:
+    """Two E2M1 codes per byte (even index in the low nibble) -> one code per byte; last dim x2."""
+    lo, hi = x & 0xF, x >> 4
+    return torch.stack([lo, hi], dim=-1).reshape(*x.shape[:-1], 2 * x.shape[-1])
+
+
+def pack_fp4(c: torch.Tensor) -> torch.Tensor:
+    """One E2M1 code per byte -> two per byte (even index in the low nibble); last dim / 2."""
+    c = c.reshape(*c.shape[:-1], c.shape[-1] // 2, 2)
+    return (c[..., 0] | (c[..., 1] << 4)).contiguous()

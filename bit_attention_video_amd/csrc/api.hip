@@ -164,6 +164,46 @@ int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uin
   return hip_status(vc_launch_attn_fwd(Q, Kq, sK, Rq, mu, sV, B * H, N, L, flags, O, stream));
 }
 
+int vc_vsmooth_demean_quant_mx4(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                int B, int H, int N, int d, unsigned flags,
+                                uint8_t* Kq4, uint8_t* sK4, uint8_t* Rq4, uint8_t* sR4,
+                                uint16_t* mu_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!K || !V || !Kq4 || !sK4 || !Rq4 || !sR4 || !mu_out || !ws) return VC_ERR_NULL;
+  if (flags & ~(VC_DQ_NO_DEMEAN | VC_DQ_HADAMARD)) return VC_ERR_FLAGS;
+  int BH = B * H;
+  vc_dq_ws L = vc_dq_ws_layout(BH, N);
+  if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
+  return hip_status(vc_launch_demean_quant_mx4(K, V, perm, BH, N, flags, Kq4, sK4, Rq4, sR4, mu_out,
+                                               (char*)ws, L, stream));
+}
+
+int vc_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4, const uint8_t* Rq4,
+                    const uint8_t* sR4, const uint16_t* mu, int B, int H, int N, int d,
+                    float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!Q || !Kq4 || !sK4 || !Rq4 || !sR4 || !O) return VC_ERR_NULL;
+  if (!mu && !(flags & VC_ATTN_NO_MEAN)) return VC_ERR_NULL;
+  if (flags & ~(VC_ATTN_NO_MEAN | VC_ATTN_HADAMARD)) return VC_ERR_FLAGS;
+  if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return VC_ERR_SHAPE;
+  // L4 = float32(log2(e) * scale), the scale taken in double (1/sqrt(d) when 0 is passed)
+  const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;
+  const float L4 = (float)(1.4426950408889634 * scale);
+  return hip_status(vc_launch_attn_fwd_mx4(Q, Kq4, sK4, Rq4, sR4, mu, B * H, N, L4, flags, O, stream));
+}
+
+int vc_test_fp4_encode(const float* x, uint8_t* codes, size_t n, hipStream_t stream) {
+  if (n == 0) return VC_OK;
+  if (!x || !codes) return VC_ERR_NULL;
+  if (n & 1) return VC_ERR_SHAPE;
+  if (n >= (size_t(1) << 40)) return VC_ERR_OVERFLOW;
+  return hip_status(vc_launch_test_fp4(x, codes, n / 2, stream));
+}
+
 int vc_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t stream) {
   if (n == 0) return VC_OK;
   if (!u || !codes) return VC_ERR_NULL;

@@ -1,0 +1,90 @@
+// Device helpers shared by the attention kernels (gfx950 only): lane-pair exchange, direct
+// global -> LDS copies, phase barriers, the bf16 matrix instruction and the query-row rotation.
+#pragma once
+
+#include "vc_common.h"
+
+namespace vc_attn {
+
+// Maximum of lanes q and q+32 (v_permlane32_swap returns both in every lane).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+// Direct global -> LDS copies (global_load_lds: lane i of the wave writes bytes
+// [base + size*i, base + size*(i+1)) of LDS, base taken from M0).  They are issued as inline
+// assembly on purpose: the compiler cannot tell the tile being filled from the tiles being
+// read, and would otherwise wait for every prefetch before the next LDS read.  Completion
+// is awaited explicitly (vmcnt) before the barrier that publishes a tile.
+// The global address is a per-lane 64-bit VGPR address.  (An SGPR base would need the five
+// wait states gfx9 requires between a vector write of an SGPR and a memory instruction that
+// reads it, which the compiler does not insert in front of inline assembly.)  The s_nop gives
+// the M0 write by the scalar unit a wait state before the copy reads it.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  const uint8_t* g = (const uint8_t*)gbase + voff;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds_base) {
+  const uint8_t* g = (const uint8_t*)gbase + voff;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+}
+// Workgroup barrier between two phases.  No LDS read needs to be complete here: every tile
+// buffer is rewritten only after the instructions that consume its reads, and the compiler
+// waits for a read before its consumer.  The copies in flight keep going.  The scheduling
+// fences keep the compiler from moving any instruction across the barrier, which would mix
+// the two phases.
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Wait until at most NOUT of this wave's copies into LDS are in flight (they complete in
+// issue order), then the barrier that publishes the completed ones.
+template <int NOUT>
+__device__ __forceinline__ void wait_dma_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NOUT) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Pins a phase's results before the barrier that ends it: the compiler may not sink the
+// instructions that produce them into the next phase (no instruction is emitted).
+template <typename T>
+__device__ __forceinline__ void keep(T& x) {
+  asm volatile("" : "+v"(x));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
+}
+
+__device__ __forceinline__ v16f mfma_bf16(v8s a, v8s b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
+                                                 0, 0, 0);
+}
+
+// Rotation of one query row by the Sylvester Hadamard matrix H (entries +-1, App. B's Q pass).
+// Lane (q, hl) holds channels 64 c + 32 hl + 8 m + j of row q as x[32 c + 8 m + j]: local index
+// bits 0-4 are channel bits 0-4, local bit 5 is channel bit 6, and channel bit 5 is the lane
+// half.  The butterflies run in float64, where the signed sum of the 128 float32 terms is exact
+// whatever the order, and each result is rounded to float32 once.
+__device__ __forceinline__ void hadamard_q_row(float* x, int hl) {
+  double y[64];
+#pragma unroll
+  for (int k = 0; k < 64; ++k) y[k] = (double)x[k];
+#pragma unroll
+  for (int b = 1; b < 64; b <<= 1)
+#pragma unroll
+    for (int k = 0; k < 64; ++k)
+      if (!(k & b)) {
+        const double u = y[k], v = y[k | b];
+        y[k] = u + v;
+        y[k | b] = u - v;
+      }
+#pragma unroll
+  for (int k = 0; k < 64; ++k) {
+    const double o = __shfl_xor(y[k], 32, 64);
+    x[k] = (float)(hl ? o - y[k] : y[k] + o);
+  }
+}
+
+}  // namespace vc_attn

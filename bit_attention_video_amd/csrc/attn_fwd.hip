@@ -53,10 +53,13 @@
 #include "vc_common.h"
 #include "vc_internal.h"
 #include "vc_attn.h"
+#include "attn_common.h"
 
 #include <type_traits>
 
 namespace {
+
+using namespace vc_attn;
 
 constexpr int TILE_BYTES = 128 * 128;
 constexpr float EC_C = 119.65f;    // 120 + beta, beta = -0.35 (Eq. 7)
@@ -70,57 +73,6 @@ constexpr int NBUF = 4;            // K and R tile buffers each (prefetch depth 
 // of a 256-byte period, so the lanes one LDS cycle serves never share a bank.
 __device__ __forceinline__ int swz_phys(int row, int c16) { return c16 ^ (row & 7) ^ ((row >> 3) & 1); }
 __device__ __forceinline__ int swz(int row, int c16) { return row * 128 + (swz_phys(row, c16) << 4); }
-
-// Maximum of lanes q and q+32 (v_permlane32_swap returns both in every lane).
-__device__ __forceinline__ float pair_max(float x) {
-  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-}
-
-// Direct global -> LDS copies (global_load_lds: lane i of the wave writes bytes
-// [base + size*i, base + size*(i+1)) of LDS, base taken from M0).  They are issued as inline
-// assembly on purpose: the compiler cannot tell the tile being filled from the tiles being
-// read, and would otherwise wait for every prefetch before the next LDS read.  Completion
-// is awaited explicitly (vmcnt) before the barrier that publishes a tile.
-// The global address is a per-lane 64-bit VGPR address.  (An SGPR base would need the five
-// wait states gfx9 requires between a vector write of an SGPR and a memory instruction that
-// reads it, which the compiler does not insert in front of inline assembly.)  The s_nop gives
-// the M0 write by the scalar unit a wait state before the copy reads it.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
-}
-// Workgroup barrier between two phases.  No LDS read needs to be complete here: every tile
-// buffer is rewritten only after the instructions that consume its reads, and the compiler
-// waits for a read before its consumer.  The copies in flight keep going.  The scheduling
-// fences keep the compiler from moving any instruction across the barrier, which would mix
-// the two phases.
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-// Wait until at most NOUT of this wave's copies into LDS are in flight (they complete in
-// issue order), then the barrier that publishes the completed ones.
-template <int NOUT>
-__device__ __forceinline__ void wait_dma_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NOUT) : "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-// Pins a phase's results before the barrier that ends it: the compiler may not sink the
-// instructions that produce them into the next phase (no instruction is emitted).
-template <typename T>
-__device__ __forceinline__ void keep(T& x) {
-  asm volatile("" : "+v"(x));
-}
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
-}
 
 // Source offset (bytes, within a 16 KB tile) of the chunk a lane copies with instruction i
 // of wave w: the instruction fills LDS chunks (2w + i) * 64 + lane of the swizzled tile, so
@@ -146,10 +98,6 @@ __device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c, int sa, int sb) {
 }
 __device__ __forceinline__ v4f mfma_fp8_16(v8i a, v8i b, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-}
-__device__ __forceinline__ v16f mfma_bf16(v8s a, v8s b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
-                                                 0, 0, 0);
 }
 
 // Constant A operand of the row-sum product D = A . B (16x16x128, FP8).  In that instruction
@@ -179,31 +127,6 @@ __device__ __forceinline__ v8i rowsum_ones(int word) {
 // ETC: P by exp-then-cast (the comparator of Sec. 3.3): the accumulator input is -m instead
 // of 119.65 - m, so the instruction returns y = a s - m, and P = E4M3_RNE(2^(y/8 + 8)) with
 // v_exp_f32 and the hardware FP8 conversion (y <= 0, so P <= 256 needs no saturation).
-// Rotation of one query row by the Sylvester Hadamard matrix H (entries +-1, App. B's Q pass).
-// Lane (q, hl) holds channels 64 c + 32 hl + 8 m + j of row q as x[32 c + 8 m + j]: local index
-// bits 0-4 are channel bits 0-4, local bit 5 is channel bit 6, and channel bit 5 is the lane
-// half.  The butterflies run in float64, where the signed sum of the 128 float32 terms is exact
-// whatever the order, and each result is rounded to float32 once.
-__device__ __forceinline__ void hadamard_q_row(float* x, int hl) {
-  double y[64];
-#pragma unroll
-  for (int k = 0; k < 64; ++k) y[k] = (double)x[k];
-#pragma unroll
-  for (int b = 1; b < 64; b <<= 1)
-#pragma unroll
-    for (int k = 0; k < 64; ++k)
-      if (!(k & b)) {
-        const double u = y[k], v = y[k | b];
-        y[k] = u + v;
-        y[k | b] = u - v;
-      }
-#pragma unroll
-  for (int k = 0; k < 64; ++k) {
-    const double o = __shfl_xor(y[k], 32, 64);
-    x[k] = (float)(hl ? o - y[k] : y[k] + o);
-  }
-}
-
 template <bool NO_MEAN, bool ETC, bool HAD>
 __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q,
                                                   const uint8_t* __restrict__ Kq,

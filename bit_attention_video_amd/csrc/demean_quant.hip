@@ -274,6 +274,157 @@ __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, 
   }
 }
 
+// ---- 4-bit path (MX E2M1 with per-32 E8M0 scales; the analogue of the pages' NVFP4 value
+// quantiser, Sec. 3.2 after Eq. 4, App. B) ----
+
+// K: per permuted row and 32-channel group, E = mx_exponent(amax), codes E2M1(x / 2^E) packed
+// two per byte (even channel in the low nibble), scale byte E + 127 (E - 7 + 127 with the
+// rotation, whose H / 128 rides on the scale).  Thread (q4, rg) takes channels 4 q4 .. 4 q4 + 3
+// of rows rg + 8 i; the eight lanes q4 = 8 G .. 8 G + 7 hold group G of a row.
+// One row's group scale and codes (see k_kquant4).
+template <bool HAD>
+__device__ __forceinline__ void kquant4_row(const float* x, int q4, size_t row, uint8_t* __restrict__ Kq4,
+                                            uint8_t* __restrict__ sK4) {
+  float a = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+  a = fmaxf(a, __shfl_xor(a, 1, 64));
+  a = fmaxf(a, __shfl_xor(a, 2, 64));
+  a = fmaxf(a, __shfl_xor(a, 4, 64));
+  const int E = mx_exponent(a);
+  const float inv = __builtin_ldexpf(1.0f, -E);   // exact
+  uint32_t w = fp4x2<0>(0u, x[0] * inv, x[1] * inv);
+  w = fp4x2<1>(w, x[2] * inv, x[3] * inv);
+  *(uint16_t*)(Kq4 + row * (VC_D / 2) + 2 * q4) = (uint16_t)w;
+  if ((q4 & 7) == 0) sK4[row * 4 + (q4 >> 3)] = (uint8_t)(E - (HAD ? 7 : 0) + 127);
+}
+
+template <bool HAD>
+__global__ __launch_bounds__(256) void k_kquant4(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
+                                                 const float* __restrict__ kbar, int N,
+                                                 uint8_t* __restrict__ Kq4, uint8_t* __restrict__ sK4) {
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, rg = t >> 5;
+  const float4 kb = *(const float4*)(kbar + (size_t)bh * VC_D + 4 * q4);
+  float x[16][4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 8 * i);
+    float v[4];
+    load4(K + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
+    x[i][0] = v[0] - kb.x;
+    x[i][1] = v[1] - kb.y;
+    x[i][2] = v[2] - kb.z;
+    x[i][3] = v[3] - kb.w;
+  }
+  const size_t row0 = (size_t)bh * N + j * VC_BLK + rg;
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) {
+    if constexpr (HAD) {   // two rows per scheduling region, as in k_kquant
+      hadamard_k_row(x[i], q4);
+      hadamard_k_row(x[i + 1], q4);
+    }
+    kquant4_row<HAD>(x[i], q4, row0 + 8 * i, Kq4, sK4);
+    kquant4_row<HAD>(x[i + 1], q4, row0 + 8 * (i + 1), Kq4, sK4);
+    if constexpr (HAD) __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+constexpr int TILE4_ROW = 72;   // LDS bytes per channel row of a 4-bit transposed tile (64 + pad)
+
+// V: per tile j and channel, the residual R = V'[pi] - mu_j in MX E2M1 over each 32-key group
+// (keys of one 64-key half with equal index bit 2, i.e. the slots 32 g .. 32 g + 31 of the PV
+// operand order), tile-transposed [channel][slot] two slots per byte; scale bytes
+// [channel][group]; mu_out = bf16(mu_j) unscaled (App. B: at 4 bits the microscales act
+// inside the matrix instruction).  Thread (q4, sub, g) takes channels 4 q4 .. 4 q4 + 3 and the
+// 16 rows 64 (g/2) + 8 a + 4 (g%2) + i4, a = 4 sub .. 4 sub + 3: slots 32 g + 16 sub + 4 (a - 4 sub)
+// + i4.  Its partner for the group maximum is lane ^ 32 (same wave, other sub).
+__global__ __launch_bounds__(256) void k_vquant4(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                 int N, const float* __restrict__ mu,
+                                                 uint8_t* __restrict__ Rq4, uint8_t* __restrict__ sR4,
+                                                 uint16_t* __restrict__ mu_out) {
+  __shared__ float mus[VC_D];
+  __shared__ __attribute__((aligned(16))) uint8_t tile[VC_D * TILE4_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t stile[VC_D * 4];
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, sub = (t >> 5) & 1, g = t >> 6;
+  const int nt = N / VC_BLK;
+  if (t < VC_D) {
+    const float m = mu[((size_t)bh * nt + j) * VC_D + t];
+    mus[t] = m;
+    mu_out[((size_t)bh * nt + j) * VC_D + t] = (uint16_t)f32_to_bf16_rne(m);
+  }
+  __syncthreads();
+  const float4 m4 = *(const float4*)(mus + 4 * q4);
+  float x[16][4];
+#pragma unroll
+  for (int aa = 0; aa < 4; ++aa)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int r = 64 * (g >> 1) + 8 * (4 * sub + aa) + 4 * (g & 1) + i4;
+      const int tok = dq_token(perm, bh, N, j * VC_BLK + r);
+      float v[4];
+      load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
+      float* xi = x[4 * aa + i4];
+      xi[0] = v[0] - m4.x;
+      xi[1] = v[1] - m4.y;
+      xi[2] = v[2] - m4.z;
+      xi[3] = v[3] - m4.w;
+    }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i][e]));
+    a = fmaxf(a, __shfl_xor(a, 32, 64));
+    const int E = mx_exponent(a);
+    const float inv = __builtin_ldexpf(1.0f, -E);
+    uint32_t w0 = 0u, w1 = 0u;
+    w0 = fp4x2<0>(w0, x[0][e] * inv, x[1][e] * inv);
+    w0 = fp4x2<1>(w0, x[2][e] * inv, x[3][e] * inv);
+    w0 = fp4x2<2>(w0, x[4][e] * inv, x[5][e] * inv);
+    w0 = fp4x2<3>(w0, x[6][e] * inv, x[7][e] * inv);
+    w1 = fp4x2<0>(w1, x[8][e] * inv, x[9][e] * inv);
+    w1 = fp4x2<1>(w1, x[10][e] * inv, x[11][e] * inv);
+    w1 = fp4x2<2>(w1, x[12][e] * inv, x[13][e] * inv);
+    w1 = fp4x2<3>(w1, x[14][e] * inv, x[15][e] * inv);
+    *(uint2*)(tile + (4 * q4 + e) * TILE4_ROW + 16 * g + 8 * sub) = make_uint2(w0, w1);
+    if (sub == 0) stile[(4 * q4 + e) * 4 + g] = (uint8_t)(E + 127);
+  }
+  __syncthreads();
+  uint8_t* dst = Rq4 + ((size_t)bh * nt + j) * (VC_D * VC_BLK / 2);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = t + 256 * k, ch = c >> 2, part = c & 3;
+    const uint2 lo = *(const uint2*)(tile + ch * TILE4_ROW + 16 * part);
+    const uint2 hi = *(const uint2*)(tile + ch * TILE4_ROW + 16 * part + 8);
+    *(uint4*)(dst + 16 * c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+  if (t < VC_D) ((uint32_t*)(sR4 + ((size_t)bh * nt + j) * (VC_D * 4)))[t] = ((const uint32_t*)stile)[t];
+}
+
+hipError_t vc_launch_demean_quant_mx4(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                      int BH, int N, unsigned flags, uint8_t* Kq4, uint8_t* sK4,
+                                      uint8_t* Rq4, uint8_t* sR4, uint16_t* mu_out, char* ws,
+                                      const vc_dq_ws& L, hipStream_t s) {
+  const int nchunk = (N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  const int nt = N / VC_BLK;
+  double* kpart = (double*)(ws + L.kpart);
+  float* kbar = (float*)(ws + L.kbar);
+  float* mu = (float*)(ws + L.mu);
+  uint32_t* amax = (uint32_t*)(ws + L.amax);
+  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
+  hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
+  if (flags & VC_DQ_HADAMARD)
+    hipLaunchKernelGGL(k_kquant4<true>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq4, sK4);
+  else
+    hipLaunchKernelGGL(k_kquant4<false>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq4, sK4);
+  // the block means (the per-channel maxima it also gathers are not used at 4 bits)
+  hipLaunchKernelGGL(k_vclear, dim3(BH), dim3(128), 0, s, amax);
+  hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(256), 0, s, V, perm, N,
+                     (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amax);
+  hipLaunchKernelGGL(k_vquant4, dim3(nt, BH), dim3(256), 0, s, V, perm, N, (const float*)mu, Rq4, sR4, mu_out);
+  return hipGetLastError();
+}
+
 hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t* perm,
                                   int BH, int N, unsigned flags, uint8_t* Kq, float* sK,
                                   uint8_t* Rq, uint16_t* mu_out, float* sV, char* ws,

@@ -1,5 +1,6 @@
-// Single-stage kernels exposed for testing: the ExpCast code (Sec. 3.3, Eq. 7) and the E4M3
-// quantiser, each with the exact instruction sequence the production kernels use.
+// Single-stage kernels exposed for testing: the ExpCast code (Sec. 3.3, Eq. 7), the E4M3
+// quantiser and the E2M1 conversion of the 4-bit path, each with the exact instruction
+// sequence the production kernels use.
 #include "vc_common.h"
 #include "vc_internal.h"
 
@@ -23,6 +24,13 @@ __global__ void k_test_e4m3(const float* __restrict__ x, uint8_t* __restrict__ c
   for (; i < n; i += stride) codes[i] = (uint8_t)(e4m3x2(x[i], 0.0f) & 0xFFu);
 }
 
+// Byte i = E2M1 codes of the pair (x[2i], x[2i+1]) as the 4-bit quantisers pack them.
+__global__ void k_test_fp4(const float* __restrict__ x, uint8_t* __restrict__ codes, size_t npair) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < npair; i += stride) codes[i] = (uint8_t)(fp4x2<0>(0u, x[2 * i], x[2 * i + 1]) & 0xFFu);
+}
+
 static unsigned grid_for(size_t n) {
   size_t g = (n + 255) / 256;
   return (unsigned)(g > 65536 ? 65536 : g);
@@ -35,5 +43,10 @@ hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipS
 
 hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s) {
   hipLaunchKernelGGL(k_test_e4m3, dim3(grid_for(n)), dim3(256), 0, s, x, codes, n);
+  return hipGetLastError();
+}
+
+hipError_t vc_launch_test_fp4(const float* x, uint8_t* codes, size_t npair, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_fp4, dim3(grid_for(npair)), dim3(256), 0, s, x, codes, npair);
   return hipGetLastError();
 }

@@ -66,6 +66,26 @@ __device__ __forceinline__ int pow2_block_exponent(float amax) {
   return E < -100 ? -100 : E;
 }
 
+// E2M1 (OCP MX FP4) codes of x0 and x1, which the caller has already divided by their power-
+// of-two group scale (|x| <= 6), written into byte SEL of `old` with x0 in the low nibble: the
+// hardware round-to-nearest-even conversion, applied with unit scale.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2(uint32_t old, float x0, float x1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, x0, x1, 1.0f, SEL);
+}
+
+// Exponent E of an MX (E8M0) group scale: the smallest power of two 2^E with amax <= 6 * 2^E,
+// 6 being E2M1's largest magnitude (0 when amax == 0, never below -100).  With
+// amax = m 2^e, m in [0.5, 1): 6 * 2^(e-3) = 0.75 * 2^e fits iff m <= 0.75, and
+// 6 * 2^(e-4) < 2^(e-1) <= amax never does.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e;
+  const float m = __builtin_frexpf(amax, &e);
+  const int E = m <= 0.75f ? e - 3 : e - 2;
+  return E < -100 ? -100 : E;
+}
+
 // Wave-wide reductions (wave64).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -31,6 +31,7 @@ constexpr int VC_KSTAT_CHUNK = 1024; // rows per key-mean partial
 
 hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t s);
 hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s);
+hipError_t vc_launch_test_fp4(const float* x, uint8_t* codes, size_t npair, hipStream_t s);
 
 hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float* C, hipStream_t s);
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
@@ -47,6 +48,16 @@ hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const in
                                   int BH, int N, unsigned flags, uint8_t* Kq, float* sK,
                                   uint8_t* Rq, uint16_t* mu_out, float* sV, char* ws,
                                   const vc_dq_ws& L, hipStream_t s);
+
+hipError_t vc_launch_demean_quant_mx4(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                      int BH, int N, unsigned flags, uint8_t* Kq4, uint8_t* sK4,
+                                      uint8_t* Rq4, uint8_t* sR4, uint16_t* mu_out, char* ws,
+                                      const vc_dq_ws& L, hipStream_t s);
+
+hipError_t vc_launch_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4,
+                                  const uint8_t* Rq4, const uint8_t* sR4, const uint16_t* mu,
+                                  int BH, int N, float L4, unsigned flags, uint16_t* O,
+                                  hipStream_t s);  // L4 = float32(log2(e) softmax_scale)
 
 hipError_t vc_launch_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK,
                               const uint8_t* Rq, const uint16_t* mu, const float* sV,

@@ -172,6 +172,48 @@ int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uin
                 float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * 4-bit V-Smooth on MX formats (Sec. 3.2 after Eq. 4: the residual goes through the host
+ * kernel's 4-bit value quantiser; Sec. 4.1 "Implementation" and App. A "Scope of ExpCast-FP8":
+ * 4 bits run V-Smooth alone, P by exponentiation; App. B: the microscales act inside the
+ * matrix instruction, so the means are added unscaled).  The pages' 4-bit format is NVFP4;
+ * MI355X's matrix instructions take MX scales, so this path uses E2M1 elements with one E8M0
+ * scale per 32 elements along each product's reduction axis.
+ *
+ * E2M1: sign, 2-bit exponent (bias 1), 1-bit mantissa; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+ * Group scale 2^E: the smallest power of two with amax <= 6 * 2^E (E >= -100, E = 0 for an
+ * all-zero group), stored as the byte E + 127; elements E2M1_RNE(x / 2^E), two per byte, the
+ * even index in the low nibble.
+ *
+ * vc_vsmooth_demean_quant_mx4: the K and V paths of vc_vsmooth_demean_quant with 4-bit outputs.
+ *   K' = float32(K[pi] - kbar) (VC_DQ_HADAMARD: float32(K' H), exponent stored minus 7);
+ *     Kq4 [B,H,N,64]: codes of each permuted row; sK4 [B,H,N,4]: the scale byte of channel
+ *     group c/32.
+ *   V' = V[pi]; mu_j = float32(block sum / 128) (0 with VC_DQ_NO_DEMEAN); R = V' - mu_j;
+ *     Rq4 [B,H,N/128][128 channels][64]: tile-transposed like Rq (slot s of channel c holds
+ *     the residual of row 128 j + key(s), two slots per byte); sR4 [B,H,N/128][128][4]: the
+ *     scale of slots 32 g .. 32 g + 31 (in key terms: the keys of one 64-key half with equal
+ *     index bit 2); mu_out bf16 [B,H,N/128,128] = bf16_RNE(mu_j), unscaled.
+ *   ws: vc_demean_quant_workspace_size(B,H,N) bytes.  flags: VC_DQ_NO_DEMEAN | VC_DQ_HADAMARD.
+ *
+ * vc_attn_fwd_mx4: per (b,h) and query row, over key tiles j of 128 permuted keys:
+ *   L4 = float32(log2(e) softmax_scale); X = float32(Q L4) (rotated by H with
+ *   VC_ATTN_HADAMARD), E2M1 per 32-channel group of the row;
+ *   S = sum over the 4 channel groups of (decoded Q x its scale)(decoded K x its scale), float32
+ *   matrix-instruction accumulation; m' = max(m, max S); P = 2^(S - m'), float32 exp2;
+ *   P in E2M1 per 32-key group (the groups of Rq4); r = sum of the dequantised P;
+ *   alpha = 2^(m - m'); A = alpha A + P Rq_j + r mu_j; l = alpha l + r; O = bf16_RNE(A / l).
+ *   flags: VC_ATTN_NO_MEAN | VC_ATTN_HADAMARD (others: VC_ERR_FLAGS); mu may be NULL only with
+ *   VC_ATTN_NO_MEAN; softmax_scale as vc_attn_fwd.
+ * -------------------------------------------------------------------------------------- */
+int vc_vsmooth_demean_quant_mx4(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                int B, int H, int N, int d, unsigned flags,
+                                uint8_t* Kq4, uint8_t* sK4, uint8_t* Rq4, uint8_t* sR4,
+                                uint16_t* mu_out, void* ws, size_t ws_bytes, hipStream_t stream);
+int vc_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4, const uint8_t* Rq4,
+                    const uint8_t* sR4, const uint16_t* mu, int B, int H, int N, int d,
+                    float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Test hooks: single stages of the path, exposed so each can be checked on its own.
  * -------------------------------------------------------------------------------------- */
 
@@ -182,6 +224,11 @@ int vc_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t stream
 /* E4M3 (OCP E4M3FN) round-to-nearest-even of float32 x, saturating to +-448, as the
  * quantisers of vc_vsmooth_demean_quant and vc_attn_fwd do it. */
 int vc_test_e4m3_encode(const float* x, uint8_t* codes, size_t n, hipStream_t stream);
+
+/* E2M1 codes of float32 pairs as the 4-bit quantisers pack them: codes[i] holds x[2i] in the
+ * low and x[2i+1] in the high nibble (round to nearest even, |x| <= 6 expected: the callers
+ * divide by the group scale first).  n (the number of floats) must be even (VC_ERR_SHAPE). */
+int vc_test_fp4_encode(const float* x, uint8_t* codes, size_t n, hipStream_t stream);
 
 /* One k-means assignment with given centroids C [B,H,k,d] float32 (the assign step of
  * vc_vsmooth_group): labels int32 [B,H,N]; mindist float32 [B,H,N] (||v - c_z||^2 as the

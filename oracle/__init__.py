@@ -19,6 +19,8 @@ Modules
   vsmooth   k-means grouping, stable label sort, K smoothing and V block
             demeaning with E4M3 quantisation (Sec. 3.2, Eq. 3-5; App. B)
   rotation  the QK Hadamard rotation fused into the Q/K quantisers (Sec. 4.1, App. B)
+  mx4       4-bit V-Smooth on MX E2M1 elements with per-32 power-of-two scales (Sec. 3.2
+            after Eq. 4, Sec. 4.1 "Implementation", App. A, App. B)
   attention exact softmax attention and the emulated tiled VC attention
             (Sec. 3.1 Eq. 1, Sec. 3.2 Eq. 6, Sec. 3.3 Eq. 7)
 
@@ -27,4 +29,4 @@ no printed worked example on the pages; it is pinned by its reductions (exact
 arithmetic -> exact attention; ExpCast row bound of Prop. 3.1; mean-restore
 identity), not by printed values.
 """
-from . import formats, expcast, analysis, rotation, vsmooth, attention  # noqa: F401
+from . import formats, expcast, analysis, rotation, vsmooth, attention, mx4  # noqa: F401

@@ -105,6 +105,42 @@ def test_demean_quant_argument_errors():
     assert f(*args(N=0)) == S["VC_OK"]
 
 
+def test_mx4_argument_errors():
+    lib = vc.lib()
+    f = lib.vc_vsmooth_demean_quant_mx4
+    ws = lib.vc_demean_quant_workspace_size(1, 2, 1024)
+    args = lambda N=1024, d=128, flags=0, K=FAKE, nws=ws, mu=FAKE: (K, FAKE, None, 1, 2, N, d, flags, FAKE, FAKE,
+                                                                    FAKE, FAKE, mu, FAKE, nws, None)
+    assert f(*args(d=64)) == S["VC_ERR_SHAPE"]
+    assert f(*args(N=200)) == S["VC_ERR_SHAPE"]
+    assert f(*args(K=None)) == S["VC_ERR_NULL"]
+    assert f(*args(mu=None)) == S["VC_ERR_NULL"]
+    assert f(*args(flags=0x4)) == S["VC_ERR_FLAGS"]
+    assert f(*args(flags=0x3, nws=ws - 1)) == S["VC_ERR_WORKSPACE"]
+    assert f(*args(N=0)) == S["VC_OK"]
+    a = lib.vc_attn_fwd_mx4
+    P = [FAKE] * 6
+    assert a(*P, 1, 1, 128, 64, 0.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert a(*P, 1, 1, 1 << 24, 128, 0.0, 0, FAKE, None) == S["VC_ERR_OVERFLOW"]
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 128, 128, 0.0, 0, FAKE, None) == S["VC_ERR_NULL"]
+    assert a(*P, 1, 1, 128, 128, 0.0, vc.VC_ATTN_EXP_THEN_CAST, FAKE, None) == S["VC_ERR_FLAGS"]   # no ExpCast at 4 bits
+    assert a(*P, 1, 1, 128, 128, -1.0, vc.VC_ATTN_HADAMARD, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 128, 128, float("inf"), 0x5, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert a(None, None, None, None, None, None, 1, 4, 0, 128, 0.0, 0, None, None) == S["VC_OK"]
+    assert lib.vc_test_fp4_encode(FAKE, FAKE, 3, None) == S["VC_ERR_SHAPE"]
+    assert lib.vc_test_fp4_encode(None, FAKE, 4, None) == S["VC_ERR_NULL"]
+    assert lib.vc_test_fp4_encode(None, None, 0, None) == S["VC_OK"]
+
+
+def test_fp4_pack_roundtrip():
+    import torch
+    c = torch.randint(0, 16, (3, 5, 128), dtype=torch.uint8)
+    p = vc.pack_fp4(c)
+    assert p.shape == (3, 5, 64)
+    assert torch.equal(vc.unpack_fp4(p), c)
+    assert int(vc.pack_fp4(torch.tensor([[1, 2]], dtype=torch.uint8))[0, 0]) == 0x21   # even index low
+
+
 def test_hook_argument_errors():
     lib = vc.lib()
     assert lib.vc_test_expcast(None, None, 0, None) == S["VC_OK"]
