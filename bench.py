@@ -25,9 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA, vendor figure
+FP4_PEAK_TFLOPS = 10100.0    # MI355X dense FP4/FP6 MFMA, vendor figure
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, vendor figure
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "attn_fwd_video_traffic.json")
-ATTN_SOURCES = ["bit_attention_video_amd/csrc/attn_fwd.hip", "bit_attention_video_amd/csrc/vc_common.h"]
+ATTN_SOURCES = ["bit_attention_video_amd/csrc/attn_fwd.hip", "bit_attention_video_amd/csrc/attn_common.h",
+                "bit_attention_video_amd/csrc/vc_common.h"]
 
 
 def attn_source_hash():
@@ -266,6 +268,26 @@ def main():
     del ops_rot
     log(f"QK rotation: demean_quant {t_dq_rot:.3f} ms, attention {t_attn_rot:.2f} ms")
 
+    # the 4-bit path (MX E2M1 operands, P by exp2): its quantisers and attention on the same pi
+    ops4 = vc.vc_vsmooth_demean_quant_mx4(Kd, Vd, g["perm"])
+    e0.record()
+    for _ in range(3):
+        ops4 = vc.vc_vsmooth_demean_quant_mx4(Kd, Vd, g["perm"])
+    e1.record()
+    torch.cuda.synchronize()
+    t_dq4 = e0.elapsed_time(e1) / 3
+    attn4 = lambda: vc.vc_attn_fwd_mx4(Qd, ops4["Kq4"], ops4["sK4"], ops4["Rq4"], ops4["sR4"], ops4["mu"], out=O)
+    attn4()
+    e0.record()
+    for _ in range(3):
+        attn4()
+    e1.record()
+    torch.cuda.synchronize()
+    t_attn4 = e0.elapsed_time(e1) / 3
+    assert torch.isfinite(O.float()).all(), "non-finite attention output (4-bit)"
+    del ops4
+    log(f"4-bit path: demean_quant {t_dq4:.3f} ms, attention {t_attn4:.2f} ms")
+
     if args.attn_only_iters:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -309,6 +331,10 @@ def main():
         "vsmooth_over_attn": {k2: round(v2, 4) for k2, v2 in amort.items()},
         "p_path": {"expcast_ms": round(t_attn, 4), "exp_then_cast_ms": round(t_etc, 4),
                    "expcast_speedup": round(t_etc / t_attn, 4)},
+        "mx4": {"demean_quant_ms": round(t_dq4, 4), "attn_ms": round(t_attn4, 4),
+                "attn_tflops": round(attn_flops(B, H, N, d) / (t_attn4 * 1e-3) / 1e12, 2),
+                "attn_frac_of_fp4_peak": round(attn_flops(B, H, N, d) / (t_attn4 * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
+                "attn_over_8bit": round(t_attn4 / t_attn, 4)},
         "qk_rotation": {"demean_quant_ms": round(t_dq_rot, 4), "attn_ms": round(t_attn_rot, 4),
                         "attn_over_unrotated": round(t_attn_rot / t_attn, 4),
                         "demean_quant_over_unrotated": round(t_dq_rot / t_dq, 4)},
