@@ -73,8 +73,15 @@ __global__ __launch_bounds__(256) void k_kstat_partial(const uint16_t* __restric
 __global__ __launch_bounds__(128) void k_kstat_final(const double* __restrict__ kpart, int N, int nchunk,
                                                      float* __restrict__ kbar) {
   const int bh = blockIdx.x, t = threadIdx.x;
-  double s = 0;
-  for (int c = 0; c < nchunk; ++c) s += kpart[((size_t)bh * nchunk + c) * VC_D + t];
+  const double* p = kpart + (size_t)bh * nchunk * VC_D + t;
+  // eight independent partial sums, so the loads are in flight together (exact either way)
+  double a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int c = 0;
+  for (; c + 8 <= nchunk; c += 8)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a[u] += p[(size_t)(c + u) * VC_D];
+  for (; c < nchunk; ++c) a[0] += p[(size_t)c * VC_D];
+  const double s = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   kbar[(size_t)bh * VC_D + t] = (float)(s / (double)N);
 }
 

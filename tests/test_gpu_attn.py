@@ -43,7 +43,7 @@ def _dev_ops(ops_list):
 
 
 @pytest.mark.parametrize("name,heads,nrows", [("tiny", None, 1024), ("medium", [0, 6], 1024),
-                                              ("video", [7], 256)])
+                                              ("video", [7], 256), ("long", [4], 128)])
 def test_attn_fwd_on_oracle_operands(name, heads, nrows):
     """Kernel alone: identical quantised operands in, compare O with the emulated recurrence."""
     cfg, Q, K, V = config_inputs(name, heads)

@@ -70,7 +70,7 @@ def test_group_one_iteration_matches_oracle(name, heads):
         assert J[0, h] == pytest.approx(S.kmeans_objective(Vh, ref_lab, ref_C), rel=1e-6)
 
 
-@pytest.mark.parametrize("name,heads", [("tiny", None), ("medium", [0, 3]), ("video", [0])])
+@pytest.mark.parametrize("name,heads", [("tiny", None), ("medium", [0, 3]), ("video", [0]), ("long", [1])])
 def test_group_full_objective_within_1e3(name, heads):
     cfg, Q, K, V = config_inputs(name, heads)
     note(f"group iters={cfg.iters} {name} heads={heads}")
