@@ -6,7 +6,8 @@
 // maxima are exact; x / s is one correctly rounded float32 division; E4M3 rounding is the
 // hardware's round-to-nearest-even conversion of a value already inside +-448.
 //
-// Passes (all grids are (blocks, b*h); 256 threads = 32 channel quads x 8 row groups):
+// Passes (all grids are (blocks, b*h); 256 or 512 threads = 32 channel quads x 8 or 16 row
+// groups):
 //   k_kstat_partial  float64 channel sums of K per 1024-row chunk
 //   k_kstat_final    kbar = float32(sum / N) in chunk order
 //   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = 2^E (smallest power of two
@@ -32,11 +33,13 @@ __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
   v[3] = bf16_to_f32(raw.y >> 16);
 }
 
-__device__ __forceinline__ float block_max_256(float v, float* red4) {
+// Maximum over a 512-thread block (8 waves).
+__device__ __forceinline__ float block_max_512(float v, float* red8) {
   v = wave_max(v);
-  if ((threadIdx.x & 63) == 0) red4[threadIdx.x >> 6] = v;
+  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+  return fmaxf(fmaxf(fmaxf(red8[0], red8[1]), fmaxf(red8[2], red8[3])),
+               fmaxf(fmaxf(red8[4], red8[5]), fmaxf(red8[6], red8[7])));
 }
 
 __global__ __launch_bounds__(256) void k_kstat_partial(const uint16_t* __restrict__ K, int N, int nchunk,
@@ -113,19 +116,21 @@ __device__ __forceinline__ void hadamard_k_row(float* x, int q4) {
 }
 
 // HAD: codes of (K[pi] - kbar) H; the stored scale is 2^(E-7), carrying the 1/128 of H / 128.
+// 512 threads per 128-row block: thread (q4, rg) takes channels 4 q4 .. 4 q4 + 3 of rows
+// rg + 16 i, i < 8 (few registers per thread, so many blocks stream at once).
 template <bool HAD>
-__global__ __launch_bounds__(256, 4) void k_kquant(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
+__global__ __launch_bounds__(512) void k_kquant(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
                                                 const float* __restrict__ kbar, int N,
                                                 uint8_t* __restrict__ Kq, float* __restrict__ sK) {
-  __shared__ float red4[4];
+  __shared__ float red8[8];
   const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
   const int q4 = t & 31, rg = t >> 5;
   const float4 kb = *(const float4*)(kbar + (size_t)bh * VC_D + 4 * q4);
-  float x[16][4];
+  float x[8][4];
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 8 * i);
+  for (int i = 0; i < 8; ++i) {
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 16 * i);
     float v[4];
     load4(K + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
     x[i][0] = v[0] - kb.x;
@@ -137,25 +142,25 @@ __global__ __launch_bounds__(256, 4) void k_kquant(const uint16_t* __restrict__ 
       for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
   }
   if constexpr (HAD) {
-    // two rows at a time: interleaving all rows' exchanges would need 16 live float64 sets
+    // two rows at a time: interleaving all rows' exchanges would need eight live float64 sets
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int i = 0; i < 8; i += 2) {
       hadamard_k_row(x[i], q4);
       hadamard_k_row(x[i + 1], q4);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
   }
-  amax = block_max_256(amax, red4);
+  amax = block_max_512(amax, red8);
   const int E = pow2_block_exponent(amax);
   const float inv = __builtin_ldexpf(1.0f, -E);   // exact: the scale is a power of two
   const float s = __builtin_ldexpf(1.0f, HAD ? E - 7 : E);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int r = j * VC_BLK + rg + 8 * i;
+  for (int i = 0; i < 8; ++i) {
+    const int r = j * VC_BLK + rg + 16 * i;
     const uint32_t w = e4m3x4(x[i][0] * inv, x[i][1] * inv, x[i][2] * inv, x[i][3] * inv);
     *(uint32_t*)(Kq + ((size_t)bh * N + r) * VC_D + 4 * q4) = w;
   }
@@ -166,19 +171,20 @@ __global__ __launch_bounds__(128) void k_vclear(uint32_t* __restrict__ amax) {
   amax[(size_t)blockIdx.x * VC_D + threadIdx.x] = 0u;
 }
 
-__global__ __launch_bounds__(256) void k_vpass1(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+// 512 threads per block: thread (q4, rg) takes channels 4 q4 .. 4 q4 + 3 of rows rg + 16 i.
+__global__ __launch_bounds__(512) void k_vpass1(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                 int N, int demean, float* __restrict__ mu,
                                                 uint32_t* __restrict__ amax) {
-  __shared__ double part[8][VC_D];
+  __shared__ double part[16][VC_D];
   __shared__ float mus[VC_D];
-  __shared__ float mx[8][VC_D];
+  __shared__ float mx[16][VC_D];
   const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
   const int q4 = t & 31, rg = t >> 5;
-  float x[16][4];
+  float x[8][4];
   double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 8 * i);
+  for (int i = 0; i < 8; ++i) {
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 16 * i);
     load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, x[i]);
     a0 += x[i][0]; a1 += x[i][1]; a2 += x[i][2]; a3 += x[i][3];
   }
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(256) void k_vpass1(const uint16_t* __restrict__ V, 
   if (t < VC_D) {
     double s = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s += part[i][t];
+    for (int i = 0; i < 16; ++i) s += part[i][t];
     const float m = demean ? (float)(s / 128.0) : 0.0f;
     mus[t] = m;
     mu[((size_t)bh * (N / VC_BLK) + j) * VC_D + t] = m;
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(256) void k_vpass1(const uint16_t* __restrict__ V, 
   for (int e = 0; e < 4; ++e) m[e] = 0.0f;
   const float4 mv = *(const float4*)(mus + 4 * q4);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < 8; ++i) {
     m[0] = fmaxf(m[0], fabsf(x[i][0] - mv.x));
     m[1] = fmaxf(m[1], fabsf(x[i][1] - mv.y));
     m[2] = fmaxf(m[2], fabsf(x[i][2] - mv.z));
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(256) void k_vpass1(const uint16_t* __restrict__ V, 
   if (t < VC_D) {
     float a = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a = fmaxf(a, mx[i][t]);
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, mx[i][t]);
     atomicMax(amax + (size_t)bh * VC_D + t, __float_as_uint(a));  // a >= 0: uint order = float order
   }
 }
@@ -426,7 +432,7 @@ hipError_t vc_launch_demean_quant_mx4(const uint16_t* K, const uint16_t* V, cons
     hipLaunchKernelGGL(k_kquant4<false>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq4, sK4);
   // the block means (the per-channel maxima it also gathers are not used at 4 bits)
   hipLaunchKernelGGL(k_vclear, dim3(BH), dim3(128), 0, s, amax);
-  hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(256), 0, s, V, perm, N,
+  hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(512), 0, s, V, perm, N,
                      (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amax);
   hipLaunchKernelGGL(k_vquant4, dim3(nt, BH), dim3(256), 0, s, V, perm, N, (const float*)mu, Rq4, sR4, mu_out);
   return hipGetLastError();
@@ -445,11 +451,11 @@ hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const in
   hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
   if (flags & VC_DQ_HADAMARD)
-    hipLaunchKernelGGL(k_kquant<true>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
+    hipLaunchKernelGGL(k_kquant<true>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
   else
-    hipLaunchKernelGGL(k_kquant<false>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
+    hipLaunchKernelGGL(k_kquant<false>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
   hipLaunchKernelGGL(k_vclear, dim3(BH), dim3(128), 0, s, amax);
-  hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(256), 0, s, V, perm, N,
+  hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(512), 0, s, V, perm, N,
                      (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amax);
   hipLaunchKernelGGL(k_vpass2, dim3(nt, BH), dim3(256), 0, s, V, perm, N, (const float*)mu,
                      (const uint32_t*)amax, Rq, mu_out, sV);
