@@ -52,7 +52,8 @@ vc_dq_ws vc_dq_ws_layout(int BH, int N) {
   L.kpart = off; off = align256(off + (size_t)BH * nchunk * 128 * sizeof(double));
   L.kbar = off;  off = align256(off + (size_t)BH * 128 * sizeof(float));
   L.mu = off;    off = align256(off + (size_t)BH * (size_t)(N / 128) * 128 * sizeof(float));
-  L.amax = off;  off = align256(off + (size_t)BH * 128 * sizeof(uint32_t));
+  L.amaxp = off; off = align256(off + (size_t)BH * (size_t)(N / 128) * 128 * sizeof(float));
+  L.amax = off;  off = align256(off + (size_t)BH * 8 * 128 * sizeof(float));
   L.total = off;
   return L;
 }

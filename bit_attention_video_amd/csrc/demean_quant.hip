@@ -13,9 +13,10 @@
 //   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = 2^E (smallest power of two
 //                    with amax <= 448 sK, an E8M0 block scale), codes; with VC_DQ_HADAMARD the
 //                    rows K' H (Sylvester H, App. B) are quantised and sK = 2^(E-7)
-//   k_vclear         zero the per-channel |R| maxima
-//   k_vpass1         per block of V[pi]: mu_j (float64 sum / 128), |R| maxima -> atomicMax
-//   k_vpass2         sV = amax/448; codes of R / sV into the tile-transposed PV operand order;
+//   k_vpass1         per block of V[pi]: mu_j (float64 sum / 128), the block's |R| maxima
+//   k_vamax          per-channel maximum over each eighth of the blocks (no atomics)
+//   k_vpass2         sV = (maximum of the eight) / 448; codes of R / sV into the tile-transposed
+//                    PV operand order;
 //                    mu~ = bf16(mu / sV)
 #include "vc_common.h"
 #include "vc_internal.h"
@@ -167,14 +168,25 @@ __global__ __launch_bounds__(512) void k_kquant(const uint16_t* __restrict__ K, 
   if (t == 0) sK[(size_t)bh * (N / VC_BLK) + j] = s;
 }
 
-__global__ __launch_bounds__(128) void k_vclear(uint32_t* __restrict__ amax) {
-  amax[(size_t)blockIdx.x * VC_D + threadIdx.x] = 0u;
+// amax[bh][g][c] = max over tiles j in slice g (of 8) of amaxp[bh][j][c]; 128 threads per
+// (slice, b*h), four maxima in flight per thread.
+__global__ __launch_bounds__(128) void k_vamax(const float* __restrict__ amaxp, int T, float* __restrict__ amax) {
+  const int g = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int j0 = (int)((long long)T * g / 8), j1 = (int)((long long)T * (g + 1) / 8);
+  const float* p = amaxp + (size_t)bh * T * VC_D + t;
+  float a[4] = {0, 0, 0, 0};
+  int j = j0;
+  for (; j + 4 <= j1; j += 4)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) a[u] = fmaxf(a[u], p[(size_t)(j + u) * VC_D]);
+  for (; j < j1; ++j) a[0] = fmaxf(a[0], p[(size_t)j * VC_D]);
+  amax[((size_t)bh * 8 + g) * VC_D + t] = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
 }
 
 // 512 threads per block: thread (q4, rg) takes channels 4 q4 .. 4 q4 + 3 of rows rg + 16 i.
 __global__ __launch_bounds__(512) void k_vpass1(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                 int N, int demean, float* __restrict__ mu,
-                                                uint32_t* __restrict__ amax) {
+                                                float* __restrict__ amaxp) {
   __shared__ double part[16][VC_D];
   __shared__ float mus[VC_D];
   __shared__ float mx[16][VC_D];
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(512) void k_vpass1(const uint16_t* __restrict__ V, 
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, mx[i][t]);
-    atomicMax(amax + (size_t)bh * VC_D + t, __float_as_uint(a));  // a >= 0: uint order = float order
+    amaxp[((size_t)bh * (N / VC_BLK) + j) * VC_D + t] = a;
   }
 }
 
@@ -235,7 +247,7 @@ constexpr int TILE_ROW = 132;   // LDS bytes per channel row of the transposed t
 
 __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                 int N, const float* __restrict__ mu,
-                                                const uint32_t* __restrict__ amax,
+                                                const float* __restrict__ amax,
                                                 uint8_t* __restrict__ Rq, uint16_t* __restrict__ mu_out,
                                                 float* __restrict__ sV) {
   __shared__ float sc[VC_D];
@@ -245,7 +257,9 @@ __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, 
   const int q4 = t & 31, rg = t >> 5;
   const int nt = N / VC_BLK;
   if (t < VC_D) {
-    const float a = __uint_as_float(amax[(size_t)bh * VC_D + t]);
+    float a = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) a = fmaxf(a, amax[((size_t)bh * 8 + g) * VC_D + t]);
     const float s = a == 0.0f ? 1.0f : a / 448.0f;
     const float m = mu[((size_t)bh * nt + j) * VC_D + t];
     sc[t] = s;
@@ -423,17 +437,16 @@ hipError_t vc_launch_demean_quant_mx4(const uint16_t* K, const uint16_t* V, cons
   double* kpart = (double*)(ws + L.kpart);
   float* kbar = (float*)(ws + L.kbar);
   float* mu = (float*)(ws + L.mu);
-  uint32_t* amax = (uint32_t*)(ws + L.amax);
+  float* amaxp = (float*)(ws + L.amaxp);
   hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
   if (flags & VC_DQ_HADAMARD)
     hipLaunchKernelGGL(k_kquant4<true>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq4, sK4);
   else
     hipLaunchKernelGGL(k_kquant4<false>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq4, sK4);
-  // the block means (the per-channel maxima it also gathers are not used at 4 bits)
-  hipLaunchKernelGGL(k_vclear, dim3(BH), dim3(128), 0, s, amax);
+  // the block means (the per-tile maxima it also writes are not used at 4 bits)
   hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(512), 0, s, V, perm, N,
-                     (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amax);
+                     (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amaxp);
   hipLaunchKernelGGL(k_vquant4, dim3(nt, BH), dim3(256), 0, s, V, perm, N, (const float*)mu, Rq4, sR4, mu_out);
   return hipGetLastError();
 }
@@ -447,17 +460,18 @@ hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const in
   double* kpart = (double*)(ws + L.kpart);
   float* kbar = (float*)(ws + L.kbar);
   float* mu = (float*)(ws + L.mu);
-  uint32_t* amax = (uint32_t*)(ws + L.amax);
+  float* amaxp = (float*)(ws + L.amaxp);
   hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
   if (flags & VC_DQ_HADAMARD)
     hipLaunchKernelGGL(k_kquant<true>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
   else
     hipLaunchKernelGGL(k_kquant<false>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
-  hipLaunchKernelGGL(k_vclear, dim3(BH), dim3(128), 0, s, amax);
+  float* amax = (float*)(ws + L.amax);
   hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(512), 0, s, V, perm, N,
-                     (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amax);
+                     (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amaxp);
+  hipLaunchKernelGGL(k_vamax, dim3(8, BH), dim3(128), 0, s, (const float*)amaxp, nt, amax);
   hipLaunchKernelGGL(k_vpass2, dim3(nt, BH), dim3(256), 0, s, V, perm, N, (const float*)mu,
-                     (const uint32_t*)amax, Rq, mu_out, sV);
+                     (const float*)amax, Rq, mu_out, sV);
   return hipGetLastError();
 }

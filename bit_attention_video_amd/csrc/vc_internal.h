@@ -21,7 +21,8 @@ struct vc_dq_ws {
   size_t kpart;     // float64 [BH][nchunk][128] key channel partial sums
   size_t kbar;      // float32 [BH][128] key channel means
   size_t mu;        // float32 [BH][N/128][128] block means
-  size_t amax;      // uint32 [BH][128] residual |R| maxima (float bits)
+  size_t amaxp;     // float32 [BH][N/128][128] per-tile residual |R| maxima
+  size_t amax;      // float32 [BH][8][128] residual |R| maxima over eight slices of the tiles
   size_t total;
 };
 vc_dq_ws vc_dq_ws_layout(int BH, int N);
