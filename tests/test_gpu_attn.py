@@ -156,3 +156,47 @@ def test_attn_fwd_empty_is_noop():
                          torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV),
                          torch.empty((1, 2, 128), device=DEV))
     assert out.shape == (1, 2, 0, 128)
+
+
+@pytest.mark.parametrize("scale", [0.5, 2.0])
+def test_attn_fwd_peaked_softmax(scale):
+    """Large softmax scales make the rows peaked and the running maximum move often (Eq. 1's
+    rescale branch on most tiles); the kernel still matches the emulated recurrence."""
+    cfg, Q, K, V = config_inputs("medium", [3])
+    note(f"peaked softmax scale={scale}")
+    N = cfg.N
+    perm = np.random.default_rng(13).permutation(N)
+    Qh, Kh, Vh = values(Q[0, 0]), values(K[0, 0]), values(V[0, 0])
+    ops = _oracle_ops(Qh, Kh, Vh, perm, scale=scale)
+    Kq, sK, Rq, mu, sV = _dev_ops([ops])
+    O = values(bf16_host_bits(vc.vc_attn_fwd(bf16_dev(Q), Kq, sK, Rq, mu, sV, softmax_scale=scale)))
+    rows = rows_sample(N, 512)
+    ref = T.attention_tiled(F.e4m3_decode(ops["qc"]), ops["sQ"], F.e4m3_decode(ops["kc"]), ops["sK"],
+                            F.e4m3_decode(ops["codes"]), ops["mu_t"], ops["sV"], scale=scale, rows=rows)
+    err = T.rel_l2(O[0, 0][rows], ref)
+    note(f"  rel-L2 vs emulated = {err:.3e}")
+    assert err < TOL
+
+
+@pytest.mark.parametrize("mag", [1e-4, 1e4])
+def test_vc_path_extreme_magnitudes(mag):
+    """Inputs scaled by 1e-4 and 1e4: the power-of-two block scales and the V scale follow, the
+    quantised operands stay bit-exact and the output matches the emulated oracle."""
+    rng = np.random.default_rng(14)
+    N = 512
+    Q = F.bf16_bits_from_value(F.bf16_round(rng.standard_normal((1, 1, N, 128)) * mag))
+    K = F.bf16_bits_from_value(F.bf16_round((rng.standard_normal((1, 1, N, 128)) + 1.0) * mag))
+    V = F.bf16_bits_from_value(F.bf16_round((rng.standard_normal((1, 1, N, 128)) + 2.0) * mag))
+    perm = rng.permutation(N).astype(np.int32)
+    Qh, Kh, Vh = values(Q[0, 0]), values(K[0, 0]), values(V[0, 0])
+    scale = 1.0 / (mag * mag * np.sqrt(128.0))   # keeps the scores O(1)
+    ops_dev = vc.vc_vsmooth_demean_quant(bf16_dev(K), bf16_dev(V), torch.from_numpy(perm[None, None]).to(DEV))
+    ops = _oracle_ops(Qh, Kh, Vh, perm, scale=scale)
+    assert np.array_equal(ops_dev["Kq"].cpu().numpy()[0, 0], ops["kc"])
+    assert np.array_equal(ops_dev["sK"].cpu().numpy()[0, 0], ops["sK"])
+    assert np.array_equal(ops_dev["sV"].cpu().numpy()[0, 0], ops["sV"])
+    O = values(bf16_host_bits(vc.vc_attn_fwd(bf16_dev(Q), ops_dev["Kq"], ops_dev["sK"], ops_dev["Rq"],
+                                             ops_dev["mu"], ops_dev["sV"], softmax_scale=float(scale))))
+    ref = T.attention_tiled(F.e4m3_decode(ops["qc"]), ops["sQ"], F.e4m3_decode(ops["kc"]), ops["sK"],
+                            F.e4m3_decode(ops["codes"]), ops["mu_t"], ops["sV"], scale=float(scale))
+    assert T.rel_l2(O[0, 0], ref) < TOL

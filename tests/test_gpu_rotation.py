@@ -122,3 +122,19 @@ def test_rotation_small_and_ragged_shapes():
                 Qh, Kh, Vh = values(Q[b, h]), values(K[b, h]), values(V[b, h])
                 ref = _emulated(_oracle_ops(Qh, Kh, Vh, perm[b, h]), np.arange(N))
                 assert T.rel_l2(O[b, h], ref) < TOL
+
+
+def test_rotated_no_mean_path():
+    """The rotation combined with the plain low-bit kernel (no mean term, unsmoothed V)."""
+    cfg, Q, K, V = config_inputs("qk_outlier", [2])
+    N = cfg.N
+    O = values(bf16_host_bits(vc.vc_attention(bf16_dev(Q), bf16_dev(K), bf16_dev(V), None, no_demean=True,
+                                              hadamard=True)))
+    Qh, Kh, Vh = values(Q[0, 0]), values(K[0, 0]), values(V[0, 0])
+    qc, sQ = S.quantize_q(Qh, hadamard=True)
+    kc, sK = S.quantize_k(Kh, np.arange(N), hadamard=True)
+    vq = S.quantize_v(Vh, np.arange(N), demean=False)
+    rows = rows_sample(N, 512)
+    ref = T.attention_tiled(F.e4m3_decode(qc), sQ, F.e4m3_decode(kc), sK, F.e4m3_decode(vq["codes"]),
+                            np.zeros_like(vq["mu_t"]), vq["sV"], rows=rows)
+    assert T.rel_l2(O[0, 0][rows], ref) < TOL
