@@ -37,7 +37,7 @@ vc_group_ws vc_group_ws_layout(int BH, int N, int k) {
   size_t kpad = (size_t)((k + 31) & ~31);
   size_t off = 0;
   L.hist = off;  off = align256(off + (size_t)BH * nblk * 256 * sizeof(int32_t));
-  L.jpart = off; off = align256(off + (size_t)BH * ((size_t)(N + 255) / 256) * sizeof(double));
+  L.jclust = off; off = align256(off + (size_t)BH * (size_t)k * sizeof(double));
   L.chi = off;   off = align256(off + (size_t)BH * kpad * VC_HEAD_DIM * sizeof(uint16_t));
   L.clo = off;   off = align256(off + (size_t)BH * kpad * VC_HEAD_DIM * sizeof(uint16_t));
   L.cnorm = off; off = align256(off + (size_t)BH * kpad * sizeof(float));
@@ -103,7 +103,7 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
   if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
   char* w = (char*)ws;
   int32_t* hist = (int32_t*)(w + L.hist);
-  double* jpart = (double*)(w + L.jpart);
+  double* jclust = (double*)(w + L.jclust);
   uint16_t* chi = (uint16_t*)(w + L.chi);
   uint16_t* clo = (uint16_t*)(w + L.clo);
   float* cnorm = (float*)(w + L.cnorm);
@@ -122,12 +122,8 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
       return hip_status(e);
     if ((e = vc_launch_label_sort(labels, BH, N, k, hist, perm, offsets, stream)) != hipSuccess)
       return hip_status(e);
-    if ((e = vc_launch_kmeans_update(V, perm, offsets, BH, N, k, C_out, stream)) != hipSuccess)
-      return hip_status(e);
-  }
-  if (objective) {
-    if ((e = vc_launch_kmeans_objective(V, labels, C_out, BH, N, k, jpart, objective, stream)) !=
-        hipSuccess)
+    double* J = it == iters - 1 ? objective : nullptr;   // J with the final labels and means
+    if ((e = vc_launch_kmeans_update(V, perm, offsets, BH, N, k, C_out, jclust, J, stream)) != hipSuccess)
       return hip_status(e);
   }
   return VC_OK;

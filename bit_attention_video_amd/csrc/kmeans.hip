@@ -11,7 +11,10 @@
 //   update    c_c = float32(sum of its rows / count), the sum in float64 in a fixed order over
 //             the rows of cluster c in sorted order (perm, offsets from the label sort); an
 //             empty cluster keeps its centroid.
-//   objective J = sum_t ||v_t - c_{z_t}||^2 in float64, fixed-order partials.
+//   objective J = sum_t ||v_t - c_{z_t}||^2 with the final labels and centroids, taken in the
+//             last update from its own sums: per cluster, sum ||v||^2 - 2 c.S + n ||c||^2 with
+//             S the exact float64 row sum and c the stored float32 centroid (no extra pass over
+//             V), then summed over the clusters in index order.
 #include "vc_common.h"
 #include "vc_internal.h"
 
@@ -157,19 +160,29 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restric
 
 // Centroid update: one workgroup per (cluster, b*h); 32 row streams x 16 lanes of 8 channels.
 // The sums are float64 sums of bf16 values (exact unless a cluster's values span more than
-// about 45 binary orders of magnitude), reduced in a fixed order.
+// about 45 binary orders of magnitude), reduced in a fixed order.  With OBJ the workgroup also
+// sums the squares of its rows and writes the cluster's objective term
+//   J_c = sum_{t in c} ||v_t||^2 - 2 c.S + n ||c||^2 = sum_{t in c} ||v_t - c||^2
+// with S the exact row sum and c the float32 centroid just stored (float64 arithmetic).
+template <bool OBJ>
 __global__ __launch_bounds__(512) void k_kmeans_update(const uint16_t* __restrict__ V,
                                                        const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ offsets,
-                                                       int N, int k, float* __restrict__ C) {
+                                                       int N, int k, float* __restrict__ C,
+                                                       double* __restrict__ jc) {
   __shared__ double part[32][VC_D];
+  __shared__ double red[512];
   const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int l8 = t & 15, st = t >> 4;
   const int beg = offsets[(size_t)bh * (k + 1) + c], end = offsets[(size_t)bh * (k + 1) + c + 1];
-  if (end <= beg) return;  // empty cluster keeps its centroid (uniform branch)
+  if (end <= beg) {  // empty cluster keeps its centroid and adds nothing to J (uniform branch)
+    if (OBJ && t == 0) jc[(size_t)bh * k + c] = 0.0;
+    return;
+  }
   const int32_t* pb = perm + (size_t)bh * N;
   const uint16_t* Vb = V + (size_t)bh * N * VC_D + 8 * l8;
   double a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  double sq = 0.0;
   // stream st takes the rows beg+st, beg+st+32, ...; its 16 lanes fetch the next 16 row
   // indices at once and share them, so 16 row loads are in flight per stream
   for (int p0 = beg + st; p0 < end; p0 += 32 * 16) {
@@ -187,57 +200,45 @@ __global__ __launch_bounds__(512) void k_kmeans_update(const uint16_t* __restric
       const uint32_t wd[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        a[2 * e] += (double)bf16_to_f32(wd[e] & 0xFFFFu);
-        a[2 * e + 1] += (double)bf16_to_f32(wd[e] >> 16);
+        const double x0 = (double)bf16_to_f32(wd[e] & 0xFFFFu), x1 = (double)bf16_to_f32(wd[e] >> 16);
+        a[2 * e] += x0;
+        a[2 * e + 1] += x1;
+        if constexpr (OBJ) sq = fma(x1, x1, fma(x0, x0, sq));
       }
     }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[st][8 * l8 + i] = a[i];
+  if constexpr (OBJ) red[t] = sq;
   __syncthreads();
   if (t < VC_D) {
     double s = 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) s += part[i][t];
-    C[((size_t)bh * k + c) * VC_D + t] = (float)(s / (double)(end - beg));
+    const double n = (double)(end - beg);
+    const float cf = (float)(s / n);
+    C[((size_t)bh * k + c) * VC_D + t] = cf;
+    if constexpr (OBJ) {
+      const double cd = (double)cf;
+      red[t] += cd * (n * cd - 2.0 * s);   // this channel's -2 c S + n c^2
+    }
   }
-}
-
-__global__ __launch_bounds__(256) void k_kmeans_objective(const uint16_t* __restrict__ V,
-                                                          const int32_t* __restrict__ labels,
-                                                          const float* __restrict__ C, int N, int k,
-                                                          double* __restrict__ jpart) {
-  __shared__ double red[256];
-  const int bh = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
-  const int q4 = t & 31, tg = t >> 5;
-  double acc = 0;
-  for (int i = tg; i < 256; i += 8) {
-    const int tok = blk * 256 + i;
-    if (tok >= N) break;
-    const int z = labels[(size_t)bh * N + tok];
-    const uint2 raw = *(const uint2*)(V + ((size_t)bh * N + tok) * VC_D + 4 * q4);
-    const float4 c = *(const float4*)(C + ((size_t)bh * k + z) * VC_D + 4 * q4);
-    const double d0 = (double)bf16_to_f32(raw.x & 0xFFFFu) - c.x;
-    const double d1 = (double)bf16_to_f32(raw.x >> 16) - c.y;
-    const double d2 = (double)bf16_to_f32(raw.y & 0xFFFFu) - c.z;
-    const double d3 = (double)bf16_to_f32(raw.y >> 16) - c.w;
-    acc += d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3;
-  }
-  red[t] = acc;
-  __syncthreads();
-  for (int off = 128; off > 0; off >>= 1) {
-    if (t < off) red[t] += red[t + off];
+  if constexpr (OBJ) {
     __syncthreads();
+    for (int off = 256; off > 0; off >>= 1) {   // fixed-order tree over the 512 terms
+      if (t < off) red[t] += red[t + off];
+      __syncthreads();
+    }
+    if (t == 0) jc[(size_t)bh * k + c] = red[0];
   }
-  if (t == 0) jpart[(size_t)bh * gridDim.x + blk] = red[0];
 }
 
-__global__ void k_kmeans_objective_final(const double* __restrict__ jpart, int nblk,
-                                         double* __restrict__ J) {
+// J per (b, h): the clusters' terms summed in index order.
+__global__ void k_kmeans_objective_final(const double* __restrict__ jc, int k, double* __restrict__ J) {
   const int bh = blockIdx.x;
   if (threadIdx.x == 0) {
     double s = 0;
-    for (int i = 0; i < nblk; ++i) s += jpart[(size_t)bh * nblk + i];
+    for (int i = 0; i < k; ++i) s += jc[(size_t)bh * k + i];
     J[bh] = s;
   }
 }
@@ -263,15 +264,13 @@ hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, in
 }
 
 hipError_t vc_launch_kmeans_update(const uint16_t* V, const int32_t* perm, const int32_t* offsets,
-                                   int BH, int N, int k, float* C, hipStream_t s) {
-  hipLaunchKernelGGL(k_kmeans_update, dim3(k, BH), dim3(512), 0, s, V, perm, offsets, N, k, C);
-  return hipGetLastError();
-}
-
-hipError_t vc_launch_kmeans_objective(const uint16_t* V, const int32_t* labels, const float* C,
-                                      int BH, int N, int k, double* jpart, double* J, hipStream_t s) {
-  const int nblk = (N + 255) / 256;
-  hipLaunchKernelGGL(k_kmeans_objective, dim3(nblk, BH), dim3(256), 0, s, V, labels, C, N, k, jpart);
-  hipLaunchKernelGGL(k_kmeans_objective_final, dim3(BH), dim3(64), 0, s, (const double*)jpart, nblk, J);
+                                   int BH, int N, int k, float* C, double* jc, double* J, hipStream_t s) {
+  if (J) {
+    hipLaunchKernelGGL(k_kmeans_update<true>, dim3(k, BH), dim3(512), 0, s, V, perm, offsets, N, k, C, jc);
+    hipLaunchKernelGGL(k_kmeans_objective_final, dim3(BH), dim3(64), 0, s, (const double*)jc, k, J);
+  } else {
+    hipLaunchKernelGGL(k_kmeans_update<false>, dim3(k, BH), dim3(512), 0, s, V, perm, offsets, N, k, C,
+                       (double*)nullptr);
+  }
   return hipGetLastError();
 }

@@ -34,6 +34,9 @@ __global__ __launch_bounds__(256) void k_sort_scan(int N, int nblk, int k, int32
   const int bh = blockIdx.x, c = threadIdx.x;
   int32_t* hb = hist + (size_t)bh * nblk * 256;
   int total = 0;
+  // both passes unrolled so each thread has 16 independent loads in flight (the loop is
+  // otherwise one global-memory round trip per tile)
+#pragma unroll 16
   for (int b = 0; b < nblk; ++b) total += hb[b * 256 + c];
   s[c] = total;
   __syncthreads();
@@ -46,6 +49,7 @@ __global__ __launch_bounds__(256) void k_sort_scan(int N, int nblk, int k, int32
   }
   int start = s[c] - total;  // exclusive
   int run = start;
+#pragma unroll 16
   for (int b = 0; b < nblk; ++b) {
     int v = hb[b * 256 + c];
     hb[b * 256 + c] = run;

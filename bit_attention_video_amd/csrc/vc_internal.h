@@ -9,7 +9,7 @@
 // Workspace layout of the grouping call (byte offsets from ws, each 256-byte aligned).
 struct vc_group_ws {
   size_t hist;      // int32 [BH][nblk][256] per-block label histograms, then scatter bases
-  size_t jpart;     // float64 [BH][N/256] objective partial sums
+  size_t jclust;    // float64 [BH][k] per-cluster objective terms
   size_t chi, clo;  // bf16 [BH][kpad][128] centroids split into hi + lo parts (kpad = k to 32)
   size_t cnorm;     // float32 [BH][kpad] squared centroid norms
   size_t total;
@@ -38,10 +38,10 @@ hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float*
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
                                    int32_t* labels, float* mindist, uint16_t* chi, uint16_t* clo,
                                    float* cn, hipStream_t s);
+// Update of the centroids from the sorted rows; with J non-null (the last round) also the
+// objective per (b,h) into J, via the per-cluster terms in jc.
 hipError_t vc_launch_kmeans_update(const uint16_t* V, const int32_t* perm, const int32_t* offsets,
-                                   int BH, int N, int k, float* C, hipStream_t s);
-hipError_t vc_launch_kmeans_objective(const uint16_t* V, const int32_t* labels, const float* C,
-                                      int BH, int N, int k, double* jpart, double* J, hipStream_t s);
+                                   int BH, int N, int k, float* C, double* jc, double* J, hipStream_t s);
 hipError_t vc_launch_label_sort(const int32_t* labels, int BH, int N, int k, int32_t* hist,
                                 int32_t* perm, int32_t* offsets, hipStream_t s);
 
