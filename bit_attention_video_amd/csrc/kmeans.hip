@@ -18,7 +18,8 @@
 #include "vc_common.h"
 #include "vc_internal.h"
 
-constexpr int KM_TOK_WG = 1024;  // tokens per assign workgroup (4 waves x 4 groups x 64)
+constexpr int KM_TOK_WG = 1024;  // tokens per assign workgroup (8 waves x 4 groups x 32)
+constexpr int KM_THREADS = 512;  // assign workgroup size
 constexpr int KM_ROW = 136;      // LDS row stride in bf16: 128 + 8 pad = 272 bytes
 
 __global__ __launch_bounds__(128) void k_kmeans_init(const uint16_t* __restrict__ V, int N, int k,
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(128) void k_kmeans_prep(const float* __restrict__ C
   }
 }
 
-__global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restrict__ V,
+__global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restrict__ V,
                                                        const uint16_t* __restrict__ phi,
                                                        const uint16_t* __restrict__ plo,
                                                        const float* __restrict__ pcn, int N, int kpad,
@@ -69,51 +70,45 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restric
   // copy the prepared centroids into the padded LDS rows (16-byte chunks)
   const uint4* ghi = (const uint4*)(phi + (size_t)bh * kpad * VC_D);
   const uint4* glo = (const uint4*)(plo + (size_t)bh * kpad * VC_D);
-  for (int i = t; i < kpad * (VC_D / 8); i += 256) {
+  for (int i = t; i < kpad * (VC_D / 8); i += KM_THREADS) {
     const int c = i >> 4, ch = i & 15;
     *(uint4*)(chi + c * KM_ROW + 8 * ch) = ghi[i];
     *(uint4*)(clo + c * KM_ROW + 8 * ch) = glo[i];
   }
-  for (int c = t; c < kpad; c += 256) cn[c] = pcn[(size_t)bh * kpad + c];
+  for (int c = t; c < kpad; c += KM_THREADS) cn[c] = pcn[(size_t)bh * kpad + c];
   __syncthreads();
 
-  // Each wave takes 64 tokens per group (two 32-token halves sharing every centroid fragment);
-  // the rows of the next group are loaded while the current one is computed.  Token indices
-  // past N are clamped (their labels are not written).
+  // Each wave takes 32 tokens per group (lane (q, g): token q, channel half g of every
+  // 16-channel chunk); the rows of the next group are loaded while the current one is
+  // computed.  Token indices past N are clamped (their labels are not written).
   const int w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
   const int nblk = kpad >> 5;
   const uint16_t* Vb = V + (size_t)bh * N * VC_D + 8 * g;
-  auto tok_of = [&](int grp, int h) { return blockIdx.x * KM_TOK_WG + grp * 256 + w * 64 + h * 32 + q; };
-  auto load_rows = [&](int grp, v8s (&vb)[2][8]) {
+  auto tok_of = [&](int grp) { return blockIdx.x * KM_TOK_WG + grp * (KM_THREADS / 2) + w * 32 + q; };
+  auto load_rows = [&](int grp, v8s (&vb)[8]) {
+    const int tok = tok_of(grp);
+    const uint16_t* vrow = Vb + (size_t)(tok < N ? tok : N - 1) * VC_D;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int tok = tok_of(grp, h);
-      const uint16_t* vrow = Vb + (size_t)(tok < N ? tok : N - 1) * VC_D;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) vb[h][c] = __builtin_bit_cast(v8s, *(const uint4*)(vrow + 16 * c));
-    }
+    for (int c = 0; c < 8; ++c) vb[c] = __builtin_bit_cast(v8s, *(const uint4*)(vrow + 16 * c));
   };
-  v8s vcur[2][8], vnext[2][8];
+  v8s vcur[8], vnext[8];
   load_rows(0, vcur);
 #pragma unroll
-  for (int grp = 0; grp < KM_TOK_WG / 256; ++grp) {
-    if (grp + 1 < KM_TOK_WG / 256) load_rows(grp + 1, vnext);
-    float best[2] = {__builtin_inff(), __builtin_inff()};
-    int bi[2] = {0, 0};
+  for (int grp = 0; grp < KM_TOK_WG / (KM_THREADS / 2); ++grp) {
+    if (grp + 1 < KM_TOK_WG / (KM_THREADS / 2)) load_rows(grp + 1, vnext);
+    float best = __builtin_inff();
+    int bi = 0;
     for (int cb = 0; cb < nblk; ++cb) {
-      v16f acc[2] = {v16f{}, v16f{}};
+      v16f acc = v16f{};
       const uint16_t* hrow = chi + (cb * 32 + q) * KM_ROW + 8 * g;
       const uint16_t* lrow = clo + (cb * 32 + q) * KM_ROW + 8 * g;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const v8bf ah = __builtin_bit_cast(v8bf, *(const v8s*)(hrow + 16 * c));
         const v8bf al = __builtin_bit_cast(v8bf, *(const v8s*)(lrow + 16 * c));
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const v8bf b = __builtin_bit_cast(v8bf, vcur[h][c]);
-          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc[h], 0, 0, 0);
-          acc[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc[h], 0, 0, 0);
-        }
+        const v8bf b = __builtin_bit_cast(v8bf, vcur[c]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
       }
       // candidates of this lane in increasing index order: ci = 32 cb + 8 m + 4 g + r
 #pragma unroll
@@ -123,38 +118,30 @@ __global__ __launch_bounds__(256) void k_kmeans_assign(const uint16_t* __restric
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int ci = cb * 32 + 8 * m + 4 * g + r;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float dist = fmaf(-2.0f, acc[h][4 * m + r], nn[r]);
-            if (dist < best[h]) { best[h] = dist; bi[h] = ci; }
-          }
+          const float dist = fmaf(-2.0f, acc[4 * m + r], nn[r]);
+          if (dist < best) { best = dist; bi = ci; }
         }
       }
     }
+    const float ob = __shfl_xor(best, 32, 64);
+    const int oi = __shfl_xor(bi, 32, 64);
+    if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    const int tok = tok_of(grp);
+    if (tok < N && g == 0) labels[(size_t)bh * N + tok] = bi;
+    if (mindist) {   // ||v||^2 + the best distance term (test output only)
+      float vn = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const float ob = __shfl_xor(best[h], 32, 64);
-      const int oi = __shfl_xor(bi[h], 32, 64);
-      if (ob < best[h] || (ob == best[h] && oi < bi[h])) { best[h] = ob; bi[h] = oi; }
-      const int tok = tok_of(grp, h);
-      if (tok < N && g == 0) labels[(size_t)bh * N + tok] = bi[h];
-      if (mindist) {   // ||v||^2 + the best distance term (test output only)
-        float vn = 0.0f;
+      for (int c = 0; c < 8; ++c)
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float x = bf16_to_f32((uint16_t)vcur[h][c][e]);
-            vn = fmaf(x, x, vn);
-          }
-        vn += __shfl_xor(vn, 32, 64);
-        if (tok < N && g == 0) mindist[(size_t)bh * N + tok] = vn + best[h];
-      }
+        for (int e = 0; e < 8; ++e) {
+          const float x = bf16_to_f32((uint16_t)vcur[c][e]);
+          vn = fmaf(x, x, vn);
+        }
+      vn += __shfl_xor(vn, 32, 64);
+      if (tok < N && g == 0) mindist[(size_t)bh * N + tok] = vn + best;
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) vcur[h][c] = vnext[h][c];
+    for (int c = 0; c < 8; ++c) vcur[c] = vnext[c];
   }
 }
 
@@ -258,7 +245,7 @@ hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, in
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int nblk = (N + KM_TOK_WG - 1) / KM_TOK_WG;
-  hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(256), lds, s, V, (const uint16_t*)chi,
+  hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V, (const uint16_t*)chi,
                      (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist);
   return hipGetLastError();
 }
