@@ -108,6 +108,34 @@ def test_group_warm_start_and_determinism():
     assert w["J"].item() <= g1["J"].item() * (1 + 1e-9)
 
 
+def test_group_empty_clusters():
+    """Four well-separated patterns of 256 rows, each periodic with period 128: the strided
+    start rows floor((c + 1/2) N / k) of centroids 2i and 2i + 1 are identical rows, every
+    token ties between them and goes to the lower index, so the odd clusters start empty
+    (they keep their centroid and add nothing to J)."""
+    rng = np.random.default_rng(7)
+    N, k = 1024, 8
+    base = 20.0 * rng.standard_normal((4, 128))
+    wiggle = rng.standard_normal((128, 128))
+    Vf = base[np.arange(N) // 256] + wiggle[np.arange(N) % 128]
+    Vb = F.bf16_bits_from_value(Vf)[None, None]
+    Vh = values(Vb[0, 0])
+    assert np.array_equal(Vh[64], Vh[192])                                    # the tie is real
+    for iters in (1, 3):
+        note(f"group with empty clusters, iters={iters}")
+        g = vc.vc_vsmooth_group(bf16_dev(Vb), k, iters)
+        lab, off, C, J = (g["labels"].cpu().numpy()[0, 0], g["offsets"].cpu().numpy()[0, 0],
+                          g["C"].cpu().numpy()[0, 0], g["J"].cpu().numpy()[0, 0])
+        ref = S.vsmooth_group(Vh, k, iters)
+        if iters == 1:
+            assert np.all(np.diff(off)[1::2] == 0)                            # odd clusters empty
+            C0 = S.kmeans_init_strided(Vh, k)
+            assert np.array_equal(C[1::2], F.fl32(C0[1::2]))                  # and keep their start
+        assert np.array_equal(lab, ref["labels"])
+        assert J == pytest.approx(ref["J"], rel=1e-6)
+        assert J == pytest.approx(S.kmeans_objective(Vh, lab, C.astype(np.float64)), rel=1e-9)
+
+
 def _oracle_perm(V, k, iters):
     return np.stack([S.vsmooth_group(values(V[0, h]), k, iters)["perm"] for h in range(V.shape[1])])[None]
 
