@@ -76,6 +76,21 @@ def cpu_baseline(cfg, Q, K, V, perm0, rows=16384):
                       f"value = 4*rows*N*d / time"}
 
 
+def measured_fp8_peak(vc, torch, workgroups=2048, iters=2000):
+    """The device's attainable dense FP8 rate: the library's FP8 matrix-instruction loop
+    (the instruction the attention kernel uses), timed with HIP events, best of three."""
+    vc.vc_test_mfma_fp8_rate(workgroups, 10)
+    best = float("inf")
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        vc.vc_test_mfma_fp8_rate(workgroups, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    return workgroups * iters * 4194304.0 / (best * 1e-3) / 1e12
+
+
 def reuse_schedule(args, cfg, vc, torch):
     """The permutation-reuse workload: V drifts over cfg.steps steps; grouping runs on the
     first step only and pi is reused (the pages' amortisation, Sec. 3.4).  Also times a
@@ -300,6 +315,8 @@ def main():
     fl = attn_flops(B, H, N, d)
     attn_tflops = fl / (t_attn * 1e-3) / 1e12
     value = fl / (ms_step * 1e-3) / 1e12
+    fp8_peak_meas = measured_fp8_peak(vc, torch)
+    log(f"measured dense FP8 rate {fp8_peak_meas:.0f} TFLOP/s (vendor figure {FP8_PEAK_TFLOPS:.0f})")
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
         with open(PROFILE_TRAFFIC) as f:
@@ -324,7 +341,9 @@ def main():
                    "B": B, "H": H, "N": N, "d": d, "k": cfg.k, "iters": cfg.iters},
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / FP8_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "k_attn_fwd", "avg_launch_ms": round(t_attn, 4)},
+                     "kernel": "k_attn_fwd", "avg_launch_ms": round(t_attn, 4),
+                     "measured_peak": round(fp8_peak_meas, 1),
+                     "frac_of_measured_peak": round(attn_tflops / fp8_peak_meas, 4)},
         "attn_ms": round(t_attn, 4), "attn_tflops": round(attn_tflops, 2),
         "group_ms": round(t_group, 4), "demean_quant_ms": round(t_dq, 4),
         "demean_quant_gbs": round(dq_bytes / (t_dq * 1e-3) / 1e9, 1),

@@ -24,7 +24,7 @@ import torch
 
 __all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_attn_fwd",
            "vc_attention", "vc_vsmooth_demean_quant_mx4", "vc_attn_fwd_mx4", "vc_attention_mx4",
-           "vc_test_fp4_encode", "unpack_fp4", "pack_fp4", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
+           "vc_test_fp4_encode", "vc_test_mfma_fp8_rate", "unpack_fp4", "pack_fp4", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
            "vc_test_label_sort", "rq_tiled_to_natural", "rq_natural_to_tiled", "LIB_PATH",
            "VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_ATTN_HADAMARD", "VC_DQ_NO_DEMEAN",
            "VC_DQ_HADAMARD", "STATUS"]
@@ -56,6 +56,7 @@ _SIGNATURES = {
     "vc_vsmooth_demean_quant_mx4": (_I, [_P, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "vc_attn_fwd_mx4": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
     "vc_test_fp4_encode": (_I, [_P, _P, _Z, _P]),
+    "vc_test_mfma_fp8_rate": (_I, [_P, _I, _I, _P]),
     "vc_test_expcast": (_I, [_P, _P, _Z, _P]),
     "vc_test_e4m3_encode": (_I, [_P, _P, _Z, _P]),
     "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
@@ -263,6 +264,14 @@ def vc_test_fp4_encode(x: torch.Tensor) -> torch.Tensor:
     codes = torch.empty(n // 2, dtype=torch.uint8, device=x.device)
     _check(lib().vc_test_fp4_encode(_ptr(x), _ptr(codes), n, _stream()), "vc_test_fp4_encode")
     return codes
+
+
+def vc_test_mfma_fp8_rate(workgroups: int, iters: int, device="cuda") -> torch.Tensor:
+    """Dense FP8 matrix-instruction loop (workgroups x iters x 4,194,304 FLOP); time it on the
+    current stream to get the attainable FP8 rate.  Returns the per-thread outputs."""
+    out = torch.empty(workgroups * 512, dtype=torch.float32, device=device)
+    _check(lib().vc_test_mfma_fp8_rate(_ptr(out), workgroups, iters, _stream()), "vc_test_mfma_fp8_rate")
+    return out
 
 
 def vc_test_expcast(u: torch.Tensor) -> torch.Tensor:

@@ -1,6 +1,7 @@
 // Single-stage kernels exposed for testing: the ExpCast code (Sec. 3.3, Eq. 7), the E4M3
 // quantiser and the E2M1 conversion of the 4-bit path, each with the exact instruction
-// sequence the production kernels use.
+// sequence the production kernels use; and a dense FP8 matrix-instruction loop that measures
+// the attainable FP8 rate of the device the attention kernel is compared against.
 #include "vc_common.h"
 #include "vc_internal.h"
 
@@ -31,6 +32,30 @@ __global__ void k_test_fp4(const float* __restrict__ x, uint8_t* __restrict__ co
   for (; i < npair; i += stride) codes[i] = (uint8_t)(fp4x2<0>(0u, x[2 * i], x[2 * i + 1]) & 0xFFu);
 }
 
+// Each wave issues iters x 4 independent 32x32x64 FP8 products (E8M0 scales 1) on constant
+// operands; one float per thread keeps the results live.  4 x 131072 FLOP per wave and
+// iteration.
+__global__ __launch_bounds__(512) void k_test_mfma_fp8_rate(float* __restrict__ out, int iters) {
+  const int t = threadIdx.x;
+  v8i a, b;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = 0x38383838 ^ (t & 7);   // E4M3 values near 1
+    b[k] = 0x30303030 + k;
+  }
+  v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
+    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 0, 0, 0, 127, 0, 127);
+    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 0, 0, 0, 127, 0, 127);
+    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 0, 0, 0, 127, 0, 127);
+  }
+  float r = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+  out[(size_t)blockIdx.x * 512 + t] = r;
+}
+
 static unsigned grid_for(size_t n) {
   size_t g = (n + 255) / 256;
   return (unsigned)(g > 65536 ? 65536 : g);
@@ -48,5 +73,10 @@ hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStre
 
 hipError_t vc_launch_test_fp4(const float* x, uint8_t* codes, size_t npair, hipStream_t s) {
   hipLaunchKernelGGL(k_test_fp4, dim3(grid_for(npair)), dim3(256), 0, s, x, codes, npair);
+  return hipGetLastError();
+}
+
+hipError_t vc_launch_test_mfma_fp8_rate(float* out, int workgroups, int iters, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_mfma_fp8_rate, dim3(workgroups), dim3(512), 0, s, out, iters);
   return hipGetLastError();
 }

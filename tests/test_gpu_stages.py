@@ -72,3 +72,12 @@ def test_label_sort_exact(H, N, k):
     for h in range(H):
         assert np.array_equal(perm[0, h], S.stable_argsort(z[0, h]))
         assert np.array_equal(off[0, h], S.cluster_offsets(z[0, h], k))
+
+
+def test_mfma_fp8_rate_hook():
+    """The FP8 matrix-instruction loop the bench times: it runs, its outputs are finite, and every
+    workgroup computes the same products."""
+    out = vc.vc_test_mfma_fp8_rate(4, 3)
+    o = out.view(4, 512).cpu()
+    assert torch.isfinite(o).all()
+    assert torch.equal(o[0], o[3])
