@@ -2,12 +2,14 @@
 //
 // Batch Lloyd per (b, h):
 //   init      c_c = V[floor((c + 1/2) N / k)] (float32)
-//   assign    z_t = argmin_c ||v_t - c_c||^2, ties to the lowest c.  The dot products v.c run
-//             on the bf16 matrix cores: v is exactly bf16, c is split into bf16 hi + lo parts
-//             (16 significant bits), two MFMAs accumulate in float32.  dist = ||c||^2 - 2 v.c;
-//             each lane keeps the best of its 16 centroids per block, one cross-lane exchange
-//             finishes the argmin.  A prep kernel splits the centroids and computes ||c||^2
-//             once per (b, h) and iteration; every assign workgroup copies them into LDS.
+//   assign    z_t = argmin_c ||v_t - c_c||^2, ties to the lowest c, taken as the argmax of
+//             v.c - ||c||^2 / 2 (the same order: ||v - c||^2 = ||v||^2 - 2 (v.c - ||c||^2/2)).
+//             The products run on the bf16 matrix cores: v is exactly bf16, c is split into
+//             bf16 hi + lo parts (16 significant bits), the accumulator starts from
+//             -||c||^2 / 2 and the MFMAs add v.c in float32; each lane keeps the best of its 16
+//             centroids per block, one cross-lane exchange finishes.  A prep kernel splits the
+//             centroids and computes -||c||^2 / 2 once per (b, h) and iteration; every assign
+//             workgroup copies them into LDS.
 //   update    c_c = float32(sum of its rows / count), the sum in float64 in a fixed order over
 //             the rows of cluster c in sorted order (perm, offsets from the label sort); an
 //             empty cluster keeps its centroid.
@@ -29,8 +31,8 @@ __global__ __launch_bounds__(128) void k_kmeans_init(const uint16_t* __restrict_
   C[((size_t)bh * k + c) * VC_D + e] = bf16_to_f32(V[((size_t)bh * N + row) * VC_D + e]);
 }
 
-// Centroids as bf16 hi + lo rows [kpad][128] and their squared norms (float32, summed over the
-// channels in order; padding rows get +inf so they never win).
+// Centroids as bf16 hi + lo rows [kpad][128] and -||c||^2 / 2 (float32, the squares summed over
+// the channels in order; padding rows get -inf so they never win).
 __global__ __launch_bounds__(128) void k_kmeans_prep(const float* __restrict__ C, int k, int kpad,
                                                      uint16_t* __restrict__ chi, uint16_t* __restrict__ clo,
                                                      float* __restrict__ cn) {
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(128) void k_kmeans_prep(const float* __restrict__ C
   if (c >= k) {   // padding row (uniform per block)
     chi[o] = 0;
     clo[o] = 0;
-    if (e == 0) cn[(size_t)bh * kpad + c] = __builtin_inff();
+    if (e == 0) cn[(size_t)bh * kpad + c] = -__builtin_inff();
     return;
   }
   const float* crow = C + ((size_t)bh * k + c) * VC_D;
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(128) void k_kmeans_prep(const float* __restrict__ C
   if (e == 0) {
     float s = 0.0f;
     for (int i = 0; i < VC_D; ++i) s = fmaf(crow[i], crow[i], s);
-    cn[(size_t)bh * kpad + c] = s;
+    cn[(size_t)bh * kpad + c] = -0.5f * s;
   }
 }
 
@@ -96,10 +98,17 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
 #pragma unroll
   for (int grp = 0; grp < KM_TOK_WG / (KM_THREADS / 2); ++grp) {
     if (grp + 1 < KM_TOK_WG / (KM_THREADS / 2)) load_rows(grp + 1, vnext);
-    float best = __builtin_inff();
+    float best = -__builtin_inff();   // max of v.c - ||c||^2 / 2
     int bi = 0;
     for (int cb = 0; cb < nblk; ++cb) {
-      v16f acc = v16f{};
+      // the accumulator starts from -||c||^2 / 2 of this lane's 16 candidates,
+      // ci = 32 cb + 8 m + 4 g + r in element 4 m + r
+      v16f acc;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float4 n4 = *(const float4*)(cn + cb * 32 + 8 * m + 4 * g);
+        acc[4 * m + 0] = n4.x; acc[4 * m + 1] = n4.y; acc[4 * m + 2] = n4.z; acc[4 * m + 3] = n4.w;
+      }
       const uint16_t* hrow = chi + (cb * 32 + q) * KM_ROW + 8 * g;
       const uint16_t* lrow = clo + (cb * 32 + q) * KM_ROW + 8 * g;
 #pragma unroll
@@ -110,25 +119,19 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
       }
-      // candidates of this lane in increasing index order: ci = 32 cb + 8 m + 4 g + r
+      // candidates of this lane in increasing index order (strict > keeps the lowest on ties)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 n4 = *(const float4*)(cn + cb * 32 + 8 * m + 4 * g);
-        const float nn[4] = {n4.x, n4.y, n4.z, n4.w};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ci = cb * 32 + 8 * m + 4 * g + r;
-          const float dist = fmaf(-2.0f, acc[4 * m + r], nn[r]);
-          if (dist < best) { best = dist; bi = ci; }
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int ci = cb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (acc[e] > best) { best = acc[e]; bi = ci; }
       }
     }
     const float ob = __shfl_xor(best, 32, 64);
     const int oi = __shfl_xor(bi, 32, 64);
-    if (ob < best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     const int tok = tok_of(grp);
     if (tok < N && g == 0) labels[(size_t)bh * N + tok] = bi;
-    if (mindist) {   // ||v||^2 + the best distance term (test output only)
+    if (mindist) {   // ||v||^2 - 2 (v.c - ||c||^2 / 2) of the winner (test output only)
       float vn = 0.0f;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
           vn = fmaf(x, x, vn);
         }
       vn += __shfl_xor(vn, 32, 64);
-      if (tok < N && g == 0) mindist[(size_t)bh * N + tok] = vn + best;
+      if (tok < N && g == 0) mindist[(size_t)bh * N + tok] = fmaf(-2.0f, best, vn);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) vcur[c] = vnext[c];

@@ -11,7 +11,7 @@ struct vc_group_ws {
   size_t hist;      // int32 [BH][nblk][256] per-block label histograms, then scatter bases
   size_t jclust;    // float64 [BH][k] per-cluster objective terms
   size_t chi, clo;  // bf16 [BH][kpad][128] centroids split into hi + lo parts (kpad = k to 32)
-  size_t cnorm;     // float32 [BH][kpad] squared centroid norms
+  size_t cnorm;     // float32 [BH][kpad] -||c||^2 / 2 per centroid (the assign accumulator start)
   size_t total;
 };
 vc_group_ws vc_group_ws_layout(int BH, int N, int k);
