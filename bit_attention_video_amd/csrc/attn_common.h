@@ -57,6 +57,38 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)p);
 }
 
+// Maxima of sixteen elements folded into two running maxima a (even pairs) and b (odd pairs):
+// the two chains alternate, so no instruction reads the result of the one just before it (a
+// dependent vector instruction waits ~9 cycles, an independent one issues every ~5.5).  With
+// INIT the chains start from the first pairs instead of reading a and b.
+template <bool INIT>
+__device__ __forceinline__ void max16_2chains(float& a, float& b, const v16f& x) {
+  if constexpr (INIT)
+    asm("v_max_f32 %0, %2, %3\n\t"
+        "v_max_f32 %1, %4, %5\n\t"
+        "v_max3_f32 %0, %0, %6, %7\n\t"
+        "v_max3_f32 %1, %1, %8, %9\n\t"
+        "v_max3_f32 %0, %0, %10, %11\n\t"
+        "v_max3_f32 %1, %1, %12, %13\n\t"
+        "v_max3_f32 %0, %0, %14, %15\n\t"
+        "v_max3_f32 %1, %1, %16, %17"
+        : "=&v"(a), "=&v"(b)
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+          "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+  else
+    asm("v_max3_f32 %0, %0, %2, %3\n\t"
+        "v_max3_f32 %1, %1, %4, %5\n\t"
+        "v_max3_f32 %0, %0, %6, %7\n\t"
+        "v_max3_f32 %1, %1, %8, %9\n\t"
+        "v_max3_f32 %0, %0, %10, %11\n\t"
+        "v_max3_f32 %1, %1, %12, %13\n\t"
+        "v_max3_f32 %0, %0, %14, %15\n\t"
+        "v_max3_f32 %1, %1, %16, %17"
+        : "+v"(a), "+v"(b)
+        : "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]), "v"(x[6]), "v"(x[7]),
+          "v"(x[8]), "v"(x[9]), "v"(x[10]), "v"(x[11]), "v"(x[12]), "v"(x[13]), "v"(x[14]), "v"(x[15]));
+}
+
 __device__ __forceinline__ v16f mfma_bf16(v8s a, v8s b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c,
                                                  0, 0, 0);

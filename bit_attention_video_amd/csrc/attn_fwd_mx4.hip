@@ -320,12 +320,14 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
       l_run += r;
       if (!NO_MEAN) push_r(r, j - 1);
     }
-    float tm = -__builtin_inff();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) tm = fmaxf(tm, s[kb][i]);
-    tm = pair_max(tm);
+    // the maxima of the two 32-value groups (PV step p: blocks 2p and 2p+1), then the row's
+    float gA, gB, hA, hB;
+    max16_2chains<true>(gA, gB, s[0]);
+    max16_2chains<false>(gA, gB, s[1]);
+    max16_2chains<true>(hA, hB, s[2]);
+    max16_2chains<false>(hA, hB, s[3]);
+    const float gmax[2] = {fmaxf(gA, gB), fmaxf(hA, hB)};
+    const float tm = pair_max(fmaxf(gmax[0], gmax[1]));
     const bool first = j == 0;
     const float delta = first ? tm : fmaxf(tm, 0.0f);
     if (first || __ballot(delta > 0.0f) != 0ull) {
@@ -350,12 +352,12 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       float e[32];
-      float a = 0.0f;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        e[k] = __builtin_amdgcn_exp2f(s[2 * p + (k >> 4)][k & 15]);
-        a = fmaxf(a, e[k]);
-      }
+      for (int k = 0; k < 32; ++k) e[k] = __builtin_amdgcn_exp2f(s[2 * p + (k >> 4)][k & 15]);
+      // the group's largest P: its largest score shifted like every score (delta is 0 where the
+      // maximum did not grow) is the very float32 its exponential came from, so one more
+      // exp2 returns that element's value (exp2 is monotonic) instead of a 32-value max
+      const float a = __builtin_amdgcn_exp2f(gmax[p] - delta);
       const int E = mx_exponent(a);
       pw[p] = pack_fp4_32(e, __builtin_ldexpf(1.0f, -E));
       sc |= (E + 127) << (8 * p);
