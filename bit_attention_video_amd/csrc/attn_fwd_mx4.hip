@@ -88,16 +88,18 @@ __device__ __forceinline__ v4i rowsum_ones4(int word) {
   return v4i{word, word, word, word};
 }
 
-// E2M1 codes of 32 values already divided by their group scale: nibble k = value k.
-__device__ __forceinline__ v4i pack_fp4_32(const float* x, float inv) {
+// E2M1 codes of 32 values x divided by their power-of-two group scale `scale`: nibble k = value
+// k.  The conversion instruction divides by its scale operand itself (bit for bit the codes of
+// x / scale, checked on the device for power-of-two scales), so no separate multiply runs.
+__device__ __forceinline__ v4i pack_fp4_32(const float* x, float scale) {
   v4i r;
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
     uint32_t w = 0u;
-    w = fp4x2<0>(w, x[8 * wd + 0] * inv, x[8 * wd + 1] * inv);
-    w = fp4x2<1>(w, x[8 * wd + 2] * inv, x[8 * wd + 3] * inv);
-    w = fp4x2<2>(w, x[8 * wd + 4] * inv, x[8 * wd + 5] * inv);
-    w = fp4x2<3>(w, x[8 * wd + 6] * inv, x[8 * wd + 7] * inv);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * wd + 0], x[8 * wd + 1], scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * wd + 2], x[8 * wd + 3], scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * wd + 4], x[8 * wd + 5], scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[8 * wd + 6], x[8 * wd + 7], scale, 3);
     r[wd] = (int)w;
   }
   return r;
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
 #pragma unroll
     for (int k = 0; k < 32; ++k) a = fmaxf(a, fabsf(qs[32 * c + k]));
     const int E = mx_exponent(a);
-    qf[c] = pack_fp4_32(&qs[32 * c], __builtin_ldexpf(1.0f, -E));
+    qf[c] = pack_fp4_32(&qs[32 * c], __builtin_ldexpf(1.0f, E));
     qsc |= (E + 127) << (8 * c);
   }
   wait_dma_barrier<0>();
@@ -359,7 +361,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
       // exp2 returns that element's value (exp2 is monotonic) instead of a 32-value max
       const float a = __builtin_amdgcn_exp2f(gmax[p] - delta);
       const int E = mx_exponent(a);
-      pw[p] = pack_fp4_32(e, __builtin_ldexpf(1.0f, -E));
+      pw[p] = pack_fp4_32(e, __builtin_ldexpf(1.0f, E));
       sc |= (E + 127) << (8 * p);
     }
     psc = sc;
