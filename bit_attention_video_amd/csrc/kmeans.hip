@@ -19,6 +19,9 @@
 //             V), then summed over the clusters in index order.
 #include "vc_common.h"
 #include "vc_internal.h"
+#include "vc_attn.h"
+
+#include <atomic>
 
 constexpr int KM_TOK_WG = 1024;  // tokens per assign workgroup (8 waves x 4 groups x 32)
 constexpr int KM_THREADS = 512;  // assign workgroup size
@@ -238,14 +241,29 @@ hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float*
   return hipGetLastError();
 }
 
+// The assign kernel's dynamic-LDS limit, raised once per device to what the largest k needs.
+// A function attribute is host-side state: setting it on every launch would also run inside a
+// caller's graph capture, where only the launches belong.
+static hipError_t assign_lds_limit() {
+  static std::atomic<unsigned long long> done{0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev < 64 ? (1ull << dev) : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const size_t lds_max = (size_t)2 * VC_MAX_K * KM_ROW * sizeof(uint16_t) + (size_t)VC_MAX_K * sizeof(float);
+  e = hipFuncSetAttribute((const void*)k_kmeans_assign, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
+
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
                                    int32_t* labels, float* mindist, uint16_t* chi, uint16_t* clo,
                                    float* cn, hipStream_t s) {
   const int kpad = (k + 31) & ~31;
   hipLaunchKernelGGL(k_kmeans_prep, dim3(kpad, BH), dim3(128), 0, s, C, k, kpad, chi, clo, cn);
   const size_t lds = (size_t)2 * kpad * KM_ROW * sizeof(uint16_t) + (size_t)kpad * sizeof(float);
-  hipError_t e = hipFuncSetAttribute((const void*)k_kmeans_assign,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = assign_lds_limit();
   if (e != hipSuccess) return e;
   const int nblk = (N + KM_TOK_WG - 1) / KM_TOK_WG;
   hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V, (const uint16_t*)chi,
