@@ -88,8 +88,10 @@ int vc_last_hip_error(void);
  *   objective out float64 [B,H]       J = sum_t ||v_t - c_{z_t}||^2 with the final labels and
  *                                     centroids (may be NULL)
  *   ws       scratch of at least vc_group_workspace_size(B,H,N,k) bytes, 256-byte aligned
- * Distances are taken from bf16 x (bf16 hi + bf16 lo split of the float32 centroid) matrix
- * products with float32 accumulation; centroid sums are float64 in a fixed order.
+ * The assignment takes the argmax of v.c - ||c||^2 / 2 (the same order as the distance),
+ * accumulated in float32 from -||c||^2 / 2 and bf16 x (bf16 hi + bf16 lo split of the float32
+ * centroid) matrix products; centroid sums are float64 in a fixed order, and J is formed in
+ * float64 from the last update's own sums (sum ||v||^2 - 2 c.S + n ||c||^2 per cluster).
  * -------------------------------------------------------------------------------------- */
 size_t vc_group_workspace_size(int B, int H, int N, int k);
 int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int iters,
