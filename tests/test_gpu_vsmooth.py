@@ -136,6 +136,30 @@ def test_group_empty_clusters():
         assert J == pytest.approx(S.kmeans_objective(Vh, lab, C.astype(np.float64)), rel=1e-9)
 
 
+def test_group_small_ragged_batched():
+    """B = 2, N = 256 (less than one 1024-token sort tile), k = 7 (centroid rows padded to 32):
+    J per (b, h) against the oracle's Lloyd, and the outputs' own consistency."""
+    rng = np.random.default_rng(11)
+    B, H, N, k, iters = 2, 2, 256, 7, 4
+    Vf = rng.standard_normal((B, H, N, 128)) + 3.0 * rng.standard_normal((B, H, 1, 128)) * (np.arange(N) % 5)[None, None, :, None]
+    Vb = F.bf16_bits_from_value(Vf)
+    g = vc.vc_vsmooth_group(bf16_dev(Vb), k, iters)
+    lab, perm, off = g["labels"].cpu().numpy(), g["perm"].cpu().numpy(), g["offsets"].cpu().numpy()
+    C, J = g["C"].cpu().numpy(), g["J"].cpu().numpy()
+    for b in range(B):
+        for h in range(H):
+            Vh = values(Vb[b, h])
+            ref = S.vsmooth_group(Vh, k, iters)
+            assert J[b, h] == pytest.approx(ref["J"], rel=1e-3)
+            z = lab[b, h]
+            assert np.all(np.diff(z[perm[b, h]]) >= 0)
+            assert sorted(perm[b, h].tolist()) == list(range(N))
+            assert np.array_equal(off[b, h], np.concatenate([[0], np.cumsum(np.bincount(z, minlength=k))]))
+            for c in np.unique(z):
+                assert np.array_equal(C[b, h, c], F.fl32(Vh[z == c].mean(0)))
+            assert J[b, h] == pytest.approx(S.kmeans_objective(Vh, z, C[b, h].astype(np.float64)), rel=1e-9)
+
+
 def _oracle_perm(V, k, iters):
     return np.stack([S.vsmooth_group(values(V[0, h]), k, iters)["perm"] for h in range(V.shape[1])])[None]
 
