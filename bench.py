@@ -76,7 +76,7 @@ def cpu_baseline(cfg, Q, K, V, perm0, rows=16384):
                       f"value = 4*rows*N*d / time"}
 
 
-def measured_fp8_peak(vc, torch, workgroups=2048, iters=2000):
+def measured_fp8_peak(vc, torch, workgroups=4096, iters=2000):
     """The device's attainable dense FP8 rate: the library's FP8 matrix-instruction loop
     (the instruction the attention kernel uses), timed with HIP events, best of three."""
     vc.vc_test_mfma_fp8_rate(workgroups, 10)

@@ -32,28 +32,32 @@ __global__ void k_test_fp4(const float* __restrict__ x, uint8_t* __restrict__ co
   for (; i < npair; i += stride) codes[i] = (uint8_t)(fp4x2<0>(0u, x[2 * i], x[2 * i + 1]) & 0xFFu);
 }
 
-// Each wave issues iters x 4 independent 32x32x64 FP8 products (E8M0 scales 1) on constant
-// operands; one float per thread keeps the results live.  4 x 131072 FLOP per wave and
+// Each wave issues iters x 4 independent 32x32x64 FP8 products (E8M0 scales 1), each on its
+// own pseudo-random operand pair: E4M3 bytes hashed from (thread, register, product) and masked
+// with 0xF7 (bit 3 cleared, so never the NaN code; magnitudes up to 240).  Data that toggles the
+// multipliers like real operands do matters: constant operands draw less power and let the
+// clock run higher.  One float per thread keeps the results live; 4 x 131072 FLOP per wave and
 // iteration.
 __global__ __launch_bounds__(512) void k_test_mfma_fp8_rate(float* __restrict__ out, int iters) {
-  const int t = threadIdx.x;
-  v8i a, b;
+  const uint32_t t = threadIdx.x + 512u * blockIdx.x;
+  v8i a0, a1, a2, a3, b0, b1, b2, b3;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
-    a[k] = 0x38383838 ^ (t & 7);   // E4M3 values near 1
-    b[k] = 0x30303030 + k;
+    auto h = [&](uint32_t i) { return (int)(((t * 2654435761u) ^ (k * 40503u + 1u) * 2246822519u ^ i * 3266489917u) & 0xF7F7F7F7u); };
+    a0[k] = h(1); a1[k] = h(2); a2[k] = h(3); a3[k] = h(4);
+    b0[k] = h(5); b1[k] = h(6); b2[k] = h(7); b3[k] = h(8);
   }
   v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int it = 0; it < iters; ++it) {
-    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c0, 0, 0, 0, 127, 0, 127);
-    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c1, 0, 0, 0, 127, 0, 127);
-    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c2, 0, 0, 0, 127, 0, 127);
-    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c3, 0, 0, 0, 127, 0, 127);
+    c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, c0, 0, 0, 0, 127, 0, 127);
+    c1 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a1, b1, c1, 0, 0, 0, 127, 0, 127);
+    c2 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a2, b2, c2, 0, 0, 0, 127, 0, 127);
+    c3 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a3, b3, c3, 0, 0, 0, 127, 0, 127);
   }
   float r = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
-  out[(size_t)blockIdx.x * 512 + t] = r;
+  out[t] = r;
 }
 
 static unsigned grid_for(size_t n) {

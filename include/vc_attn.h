@@ -247,7 +247,8 @@ int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_
 /* Dense FP8 matrix-instruction rate, for quoting the attention kernel's fraction of the FP8
  * peak this device actually attains beside the vendor figure: `workgroups` workgroups of 512
  * threads, each of whose 8 waves issues `iters` x 4 independent 32x32x64 E4M3 products (the
- * instruction vc_attn_fwd uses), i.e. workgroups x iters x 4,194,304 FLOP.  The caller times
+ * instruction vc_attn_fwd uses) on fixed pseudo-random operands (data that toggles the
+ * multipliers as real operands do), i.e. workgroups x iters x 4,194,304 FLOP.  The caller times
  * the call on `stream`.  out: device float32 [workgroups * 512], written (one value per
  * thread keeps the products live).  VC_ERR_NULL for a null out, VC_ERR_SHAPE for
  * workgroups < 1, iters < 1 or a FLOP count beyond 2^62. */

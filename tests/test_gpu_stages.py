@@ -75,9 +75,9 @@ def test_label_sort_exact(H, N, k):
 
 
 def test_mfma_fp8_rate_hook():
-    """The FP8 matrix-instruction loop the bench times: it runs, its outputs are finite, and every
-    workgroup computes the same products."""
-    out = vc.vc_test_mfma_fp8_rate(4, 3)
-    o = out.view(4, 512).cpu()
-    assert torch.isfinite(o).all()
-    assert torch.equal(o[0], o[3])
+    """The FP8 matrix-instruction loop the bench times: it runs, its outputs are finite and the
+    same on a second call."""
+    o1 = vc.vc_test_mfma_fp8_rate(4, 3).cpu()
+    o2 = vc.vc_test_mfma_fp8_rate(4, 3).cpu()
+    assert torch.isfinite(o1).all()
+    assert torch.equal(o1, o2)
