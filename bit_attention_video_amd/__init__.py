@@ -56,7 +56,7 @@ _SIGNATURES = {
     "vc_vsmooth_demean_quant_mx4": (_I, [_P, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "vc_attn_fwd_mx4": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
     "vc_test_fp4_encode": (_I, [_P, _P, _Z, _P]),
-    "vc_test_mfma_fp8_rate": (_I, [_P, _I, _I, _P]),
+    "vc_test_mfma_fp8_rate": (_I, [_P, _I, _I, _P, _P]),
     "vc_test_expcast": (_I, [_P, _P, _Z, _P]),
     "vc_test_e4m3_encode": (_I, [_P, _P, _Z, _P]),
     "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
@@ -266,12 +266,15 @@ def vc_test_fp4_encode(x: torch.Tensor) -> torch.Tensor:
     return codes
 
 
-def vc_test_mfma_fp8_rate(workgroups: int, iters: int, device="cuda") -> torch.Tensor:
+def vc_test_mfma_fp8_rate(workgroups: int, iters: int, device="cuda", clock: bool = False):
     """Dense FP8 matrix-instruction loop (workgroups x iters x 4,194,304 FLOP); time it on the
-    current stream to get the attainable FP8 rate.  Returns the per-thread outputs."""
+    current stream to get the attainable FP8 rate.  Returns the per-thread outputs, and with
+    clock=True also the shader clock (MHz) each workgroup's first wave sustained in its loop."""
     out = torch.empty(workgroups * 512, dtype=torch.float32, device=device)
-    _check(lib().vc_test_mfma_fp8_rate(_ptr(out), workgroups, iters, _stream()), "vc_test_mfma_fp8_rate")
-    return out
+    mhz = torch.empty(workgroups, dtype=torch.float32, device=device) if clock else None
+    _check(lib().vc_test_mfma_fp8_rate(_ptr(out), workgroups, iters, _ptr(mhz) if clock else None, _stream()),
+           "vc_test_mfma_fp8_rate")
+    return (out, mhz) if clock else out
 
 
 def vc_test_expcast(u: torch.Tensor) -> torch.Tensor:

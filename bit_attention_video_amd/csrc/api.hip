@@ -201,11 +201,11 @@ int vc_test_fp4_encode(const float* x, uint8_t* codes, size_t n, hipStream_t str
   return hip_status(vc_launch_test_fp4(x, codes, n / 2, stream));
 }
 
-int vc_test_mfma_fp8_rate(float* out, int workgroups, int iters, hipStream_t stream) {
+int vc_test_mfma_fp8_rate(float* out, int workgroups, int iters, float* clock_mhz, hipStream_t stream) {
   if (!out) return VC_ERR_NULL;
   if (workgroups < 1 || iters < 1) return VC_ERR_SHAPE;
   if ((double)workgroups * (double)iters * 4194304.0 > 4.611686018427388e18) return VC_ERR_SHAPE;
-  return hip_status(vc_launch_test_mfma_fp8_rate(out, workgroups, iters, stream));
+  return hip_status(vc_launch_test_mfma_fp8_rate(out, workgroups, iters, clock_mhz, stream));
 }
 
 int vc_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t stream) {

@@ -37,8 +37,11 @@ __global__ void k_test_fp4(const float* __restrict__ x, uint8_t* __restrict__ co
 // with 0xF7 (bit 3 cleared, so never the NaN code; magnitudes up to 240).  Data that toggles the
 // multipliers like real operands do matters: constant operands draw less power and let the
 // clock run higher.  One float per thread keeps the results live; 4 x 131072 FLOP per wave and
-// iteration.
-__global__ __launch_bounds__(512) void k_test_mfma_fp8_rate(float* __restrict__ out, int iters) {
+// iteration.  With clock_mhz, wave 0 of each workgroup also reads the shader-cycle counter
+// (s_memtime) and the constant-rate counter (s_memrealtime, wall_mhz ticks per microsecond)
+// around its loop and writes the shader clock they imply.
+__global__ __launch_bounds__(512) void k_test_mfma_fp8_rate(float* __restrict__ out, int iters,
+                                                            float* __restrict__ clock_mhz, float wall_mhz) {
   const uint32_t t = threadIdx.x + 512u * blockIdx.x;
   v8i a0, a1, a2, a3, b0, b1, b2, b3;
 #pragma unroll
@@ -47,6 +50,13 @@ __global__ __launch_bounds__(512) void k_test_mfma_fp8_rate(float* __restrict__ 
     a0[k] = h(1); a1[k] = h(2); a2[k] = h(3); a3[k] = h(4);
     b0[k] = h(5); b1[k] = h(6); b2[k] = h(7); b3[k] = h(8);
   }
+  uint64_t c_beg = 0, w_beg = 0;
+  if (clock_mhz) {
+    w_beg = wall_clock64();
+    c_beg = clock64();
+  }
+  // the operands reach the loop only through this fence, so no product starts before the stamps
+  asm volatile("" : "+v"(a0), "+v"(a1), "+v"(a2), "+v"(a3));
   v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
   for (int it = 0; it < iters; ++it) {
     c0 = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a0, b0, c0, 0, 0, 0, 127, 0, 127);
@@ -57,6 +67,13 @@ __global__ __launch_bounds__(512) void k_test_mfma_fp8_rate(float* __restrict__ 
   float r = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+  if (clock_mhz) {
+    asm volatile("" ::"v"(r));   // every product has completed before the end stamps
+    const uint64_t c_end = clock64(), w_end = wall_clock64();
+    if (threadIdx.x == 0)
+      clock_mhz[blockIdx.x] =
+          w_end > w_beg ? (float)((double)(c_end - c_beg) / (double)(w_end - w_beg) * (double)wall_mhz) : 0.0f;
+  }
   out[t] = r;
 }
 
@@ -80,7 +97,17 @@ hipError_t vc_launch_test_fp4(const float* x, uint8_t* codes, size_t npair, hipS
   return hipGetLastError();
 }
 
-hipError_t vc_launch_test_mfma_fp8_rate(float* out, int workgroups, int iters, hipStream_t s) {
-  hipLaunchKernelGGL(k_test_mfma_fp8_rate, dim3(workgroups), dim3(512), 0, s, out, iters);
+hipError_t vc_launch_test_mfma_fp8_rate(float* out, int workgroups, int iters, float* clock_mhz,
+                                        hipStream_t s) {
+  float wall_mhz = 0.0f;
+  if (clock_mhz) {   // the constant-rate counter's frequency (kHz)
+    int dev = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return e;
+    if (khz <= 0) return hipErrorInvalidValue;
+    wall_mhz = (float)khz * 1e-3f;
+  }
+  hipLaunchKernelGGL(k_test_mfma_fp8_rate, dim3(workgroups), dim3(512), 0, s, out, iters, clock_mhz, wall_mhz);
   return hipGetLastError();
 }

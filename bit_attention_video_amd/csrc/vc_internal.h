@@ -33,7 +33,8 @@ constexpr int VC_KSTAT_CHUNK = 1024; // rows per key-mean partial
 hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t s);
 hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s);
 hipError_t vc_launch_test_fp4(const float* x, uint8_t* codes, size_t npair, hipStream_t s);
-hipError_t vc_launch_test_mfma_fp8_rate(float* out, int workgroups, int iters, hipStream_t s);
+hipError_t vc_launch_test_mfma_fp8_rate(float* out, int workgroups, int iters, float* clock_mhz,
+                                        hipStream_t s);
 
 hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float* C, hipStream_t s);
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,

@@ -250,9 +250,13 @@ int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_
  * instruction vc_attn_fwd uses) on fixed pseudo-random operands (data that toggles the
  * multipliers as real operands do), i.e. workgroups x iters x 4,194,304 FLOP.  The caller times
  * the call on `stream`.  out: device float32 [workgroups * 512], written (one value per
- * thread keeps the products live).  VC_ERR_NULL for a null out, VC_ERR_SHAPE for
- * workgroups < 1, iters < 1 or a FLOP count beyond 2^62. */
-int vc_test_mfma_fp8_rate(float* out, int workgroups, int iters, hipStream_t stream);
+ * thread keeps the products live).  clock_mhz: NULL, or device float32 [workgroups] that
+ * receives, per workgroup, the shader clock in MHz over its first wave's loop (shader-cycle
+ * counter over the constant-rate counter, scaled by hipDeviceAttributeWallClockRate): the
+ * clock the matrix unit sustained.  VC_ERR_NULL for a null out, VC_ERR_SHAPE for
+ * workgroups < 1, iters < 1 or a FLOP count beyond 2^62, VC_ERR_HIP if the counter rate
+ * cannot be read. */
+int vc_test_mfma_fp8_rate(float* out, int workgroups, int iters, float* clock_mhz, hipStream_t stream);
 
 #ifdef __cplusplus
 }

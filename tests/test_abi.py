@@ -130,10 +130,10 @@ def test_mx4_argument_errors():
     assert lib.vc_test_fp4_encode(FAKE, FAKE, 3, None) == S["VC_ERR_SHAPE"]
     assert lib.vc_test_fp4_encode(None, FAKE, 4, None) == S["VC_ERR_NULL"]
     assert lib.vc_test_fp4_encode(None, None, 0, None) == S["VC_OK"]
-    assert lib.vc_test_mfma_fp8_rate(None, 1, 1, None) == S["VC_ERR_NULL"]
-    assert lib.vc_test_mfma_fp8_rate(FAKE, 0, 1, None) == S["VC_ERR_SHAPE"]
-    assert lib.vc_test_mfma_fp8_rate(FAKE, 1, 0, None) == S["VC_ERR_SHAPE"]
-    assert lib.vc_test_mfma_fp8_rate(FAKE, 2 ** 31 - 1, 2 ** 31 - 1, None) == S["VC_ERR_SHAPE"]
+    assert lib.vc_test_mfma_fp8_rate(None, 1, 1, None, None) == S["VC_ERR_NULL"]
+    assert lib.vc_test_mfma_fp8_rate(FAKE, 0, 1, None, None) == S["VC_ERR_SHAPE"]
+    assert lib.vc_test_mfma_fp8_rate(FAKE, 1, 0, None, None) == S["VC_ERR_SHAPE"]
+    assert lib.vc_test_mfma_fp8_rate(FAKE, 2 ** 31 - 1, 2 ** 31 - 1, FAKE, None) == S["VC_ERR_SHAPE"]
 
 
 def test_fp4_pack_roundtrip():

@@ -78,6 +78,10 @@ def test_mfma_fp8_rate_hook():
     """The FP8 matrix-instruction loop the bench times: it runs, its outputs are finite and the
     same on a second call."""
     o1 = vc.vc_test_mfma_fp8_rate(4, 3).cpu()
-    o2 = vc.vc_test_mfma_fp8_rate(4, 3).cpu()
+    o2, mhz = vc.vc_test_mfma_fp8_rate(4, 3, clock=True)
     assert torch.isfinite(o1).all()
-    assert torch.equal(o1, o2)
+    assert torch.equal(o1, o2.cpu())   # the clock stamps change nothing in the products
+    # a loop long enough for the counters to resolve: a shader clock within MI355X's range
+    _, mhz = vc.vc_test_mfma_fp8_rate(256, 500, clock=True)
+    mhz = mhz.cpu()
+    assert ((mhz > 300.0) & (mhz < 3000.0)).all(), mhz
