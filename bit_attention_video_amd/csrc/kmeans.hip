@@ -9,7 +9,9 @@
 //             -||c||^2 / 2 and the MFMAs add v.c in float32; each lane keeps the best of its 16
 //             centroids per block, one cross-lane exchange finishes.  A prep kernel splits the
 //             centroids and computes -||c||^2 / 2 once per (b, h) and iteration; every assign
-//             workgroup copies them into LDS.
+//             workgroup copies them into LDS.  Two centroid blocks are processed together so
+//             that consecutive products belong to independent chains, and each block's best
+//             candidate comes from a depth-4 comparison tree.
 //   update    c_c = float32(sum of its rows / count), the sum in float64 in a fixed order over
 //             the rows of cluster c in sorted order (perm, offsets from the label sort); an
 //             empty cluster keeps its centroid.
@@ -103,31 +105,72 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
     if (grp + 1 < KM_TOK_WG / (KM_THREADS / 2)) load_rows(grp + 1, vnext);
     float best = -__builtin_inff();   // max of v.c - ||c||^2 / 2
     int bi = 0;
-    for (int cb = 0; cb < nblk; ++cb) {
-      // the accumulator starts from -||c||^2 / 2 of this lane's 16 candidates,
-      // ci = 32 cb + 8 m + 4 g + r in element 4 m + r
-      v16f acc;
+    // Block cb's accumulator starts from -||c||^2 / 2 of this lane's 16 candidates,
+    // ci = 32 cb + 8 m + 4 g + r in element 4 m + r.
+    auto init = [&](int cb) {
+      v16f a;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float4 n4 = *(const float4*)(cn + cb * 32 + 8 * m + 4 * g);
-        acc[4 * m + 0] = n4.x; acc[4 * m + 1] = n4.y; acc[4 * m + 2] = n4.z; acc[4 * m + 3] = n4.w;
+        a[4 * m + 0] = n4.x; a[4 * m + 1] = n4.y; a[4 * m + 2] = n4.z; a[4 * m + 3] = n4.w;
       }
-      const uint16_t* hrow = chi + (cb * 32 + q) * KM_ROW + 8 * g;
-      const uint16_t* lrow = clo + (cb * 32 + q) * KM_ROW + 8 * g;
+      return a;
+    };
+    auto frag = [&](const uint16_t* tab, int cb, int c) {
+      return __builtin_bit_cast(v8bf, *(const v8s*)(tab + (cb * 32 + q) * KM_ROW + 8 * g + 16 * c));
+    };
+    // The best of a block's 16 candidates by a depth-4 tree in which the higher-index side wins
+    // only when strictly larger: the maximum, and among equal maxima the lowest candidate, as a
+    // scan in index order finds (for finite distances).  Then merged into the running best,
+    // the blocks taken in index order.
+    auto block_best = [&](const v16f& a, int cb) {
+      float v[8];
+      int e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const bool gt = a[2 * i + 1] > a[2 * i];
+        v[i] = gt ? a[2 * i + 1] : a[2 * i];
+        e[i] = gt ? 2 * i + 1 : 2 * i;
+      }
+#pragma unroll
+      for (int n = 4; n >= 1; n >>= 1)
+#pragma unroll
+        for (int i = 0; i < n; ++i) {
+          const bool gt = v[2 * i + 1] > v[2 * i];
+          v[i] = gt ? v[2 * i + 1] : v[2 * i];
+          e[i] = gt ? e[2 * i + 1] : e[2 * i];
+        }
+      if (v[0] > best) {
+        best = v[0];
+        bi = cb * 32 + 4 * g + e[0] + 4 * (e[0] >> 2);   // element 4 m + r -> 8 m + 4 g + r
+      }
+    };
+    // Two blocks at a time: their product chains are independent, so the matrix unit never waits
+    // for the previous product of the same chain.  Each block's own sum runs in the same order
+    // (-||c||^2/2, then hi and lo of chunk 0, hi and lo of chunk 1, ...).
+    int cb = 0;
+    for (; cb + 1 < nblk; cb += 2) {
+      v16f a0 = init(cb), a1 = init(cb + 1);
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const v8bf ah = __builtin_bit_cast(v8bf, *(const v8s*)(hrow + 16 * c));
-        const v8bf al = __builtin_bit_cast(v8bf, *(const v8s*)(lrow + 16 * c));
         const v8bf b = __builtin_bit_cast(v8bf, vcur[c]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb, c), b, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb + 1, c), b, a1, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb, c), b, a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb + 1, c), b, a1, 0, 0, 0);
       }
-      // candidates of this lane in increasing index order (strict > keeps the lowest on ties)
+      block_best(a0, cb);
+      block_best(a1, cb + 1);
+    }
+    if (cb < nblk) {   // an odd last block (uniform)
+      v16f a0 = init(cb);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int ci = cb * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (acc[e] > best) { best = acc[e]; bi = ci; }
+      for (int c = 0; c < 8; ++c) {
+        const v8bf b = __builtin_bit_cast(v8bf, vcur[c]);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb, c), b, a0, 0, 0, 0);
+        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb, c), b, a0, 0, 0, 0);
       }
+      block_best(a0, cb);
     }
     const float ob = __shfl_xor(best, 32, 64);
     const int oi = __shfl_xor(bi, 32, 64);
