@@ -112,13 +112,14 @@ __device__ __forceinline__ int rowsum_ones_word(int lane) {
   const bool one = (G & 1) ? (i == 4 || i == 12) : (i == 0 || i == 8);
   return one ? 0x38383838 : 0;   // four E4M3 1.0
 }
-// The operand itself, rebuilt where it is used from the one register that holds its word
-// (opaque, so the compiler does not keep eight copies alive across the loop).
-__device__ __forceinline__ v8i rowsum_ones(int word) {
-  asm volatile("" : "+v"(word));
+// The operand itself: eight copies of the lane's word, built once and kept in registers for
+// the whole key loop (opaque, so the compiler keeps it rather than rebuilding it per tile).
+__device__ __forceinline__ v8i rowsum_ones(int lane) {
+  const int word = rowsum_ones_word(lane);
   v8i r;
 #pragma unroll
   for (int k = 0; k < 8; ++k) r[k] = word;
+  asm volatile("" : "+v"(r));
   return r;
 }
 
@@ -238,8 +239,11 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     }
   wait_dma_barrier<0>();   // the first copies have landed
 
-  const int ones_word = rowsum_ones_word(lane);
+  const v8i ones = rowsum_ones(lane);
   float b = 0.0f, l_run = 0.0f;   // b = 119.65 - m; set on the first tile
+  // b in every element: the QK accumulator input, kept in registers and rebuilt only when b
+  // changes (a running-maximum update), not once per tile
+  v16f bsplat = {};
   // E8M0 exponent of sK of the tile of this wave's next QK product.  It is read in the vector
   // phase before: a scalar load shares its wait counter with the LDS reads, and waiting for it
   // inside the matrix phase would also wait for every fragment in flight.
@@ -333,14 +337,10 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       for (int p = 0; p < 2; ++p)
 #pragma unroll
         for (int db = 0; db < 4; ++db) acc[db] = mfma_fp8(rf[4 * p + db], pw[p], acc[db], 127, 127);
-      const v8i ones = rowsum_ones(ones_word);
       rs = mfma_fp8_16(ones, pw[0], v4f{});
       rs = mfma_fp8_16(ones, pw[1], rs);
     }
     if constexpr (QK) {
-      v16f bsplat;   // b in every element: the accumulator input, live until issued
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bsplat[i] = b;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         s[kb] = mfma_fp8(kf[2 * kb], qf[0], bsplat, sa, sb);
@@ -417,6 +417,9 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
           for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
       }
       b -= delta;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bsplat[i] = b;
+      asm volatile("" : "+v"(bsplat));   // opaque: kept, not rebuilt from b where it is used
     }
     // ExpCast Round + clip: one saturating RNE byte conversion per element.  Byte jj of the
     // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
