@@ -13,8 +13,9 @@
 // opposite phases separated by workgroup barriers (group 0: M(j) | V(j), group 1:
 // V(j-1) | M(j)).  A SIMD holds one wave of each group, so while one of them keeps the
 // matrix unit busy the other does the vector work; with one workgroup per CU nothing else
-// competes.  K and R tiles are copied three steps ahead into four-deep LDS rings; each wave
-// issues its share of the copies in its vector phase, away from the matrix instructions.
+// competes.  K and R tiles are copied three steps ahead into a four-deep LDS ring whose slots
+// hold a K and an R tile side by side; each wave issues its share of the copies in its vector
+// phase, away from the matrix instructions.
 //
 // Layouts.  Both products use the FP8 32x32x64 matrix instruction with the key index as the
 // reduction dimension of PV, computed transposed so one lane owns one query row:
@@ -83,15 +84,6 @@ __device__ __forceinline__ int stage_src(int w, int i, int lane) {
   return row * 128 + (swz_phys(row, P & 7) << 4);
 }
 
-__device__ __forceinline__ v8i lds_frag32(const uint8_t* tile, int row, int c16) {
-  const uint4 lo = *(const uint4*)(tile + swz(row, c16));
-  const uint4 hi = *(const uint4*)(tile + swz(row, c16 + 1));
-  v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
-  return r;
-}
-
 // E4M3 x E4M3 -> float32, operands scaled by 2^(sa-127) and 2^(sb-127) (E8M0 block scales).
 __device__ __forceinline__ v16f mfma_fp8(v8i a, v8i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
@@ -136,8 +128,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
                                                   const uint16_t* __restrict__ mu,
                                                   const float* __restrict__ sV, int N, int nqb,
                                                   int nwb, uint32_t G, float L, uint16_t* __restrict__ O) {
-  __shared__ __attribute__((aligned(1024))) uint8_t kt[NBUF][TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t rt[NBUF][TILE_BYTES];
+  // ring slot s holds K tile at tiles[s][0] and R tile at tiles[s][1]: one slot base serves both
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[NBUF][2][TILE_BYTES];
   __shared__ __attribute__((aligned(256))) uint16_t mring[MRING][128];
   // first-half row sums of each query row, and b at the time they were saved
   __shared__ __attribute__((aligned(16))) float rsnap[NWAVE * 32][12];
@@ -159,7 +151,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
 
   // this wave's share of every tile copy: per-lane source offsets, LDS chunk offsets
   const uint32_t so0 = stage_src(w, 0, lane), so1 = stage_src(w, 1, lane);
-  const uint32_t kt0 = lds_addr(&kt[0][0]) + 2 * w * 1024, rt0 = lds_addr(&rt[0][0]) + 2 * w * 1024;
+  const uint32_t kt0 = lds_addr(&tiles[0][0][0]) + 2 * w * 1024, rt0 = kt0 + TILE_BYTES;
   auto stage = [&](const uint8_t* gtile, uint32_t lbase) {
     dma16(gtile, so0, lbase);
     dma16(gtile, so1, lbase + 1024);
@@ -176,8 +168,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   };
   auto clampT = [&](int i) { return i < T ? i : T - 1; };
   auto issue = [&](int j) {
-    stage(Kh + (size_t)clampT(j + D) * TILE_BYTES, kt0 + ((j + D) % NBUF) * TILE_BYTES);
-    stage(Rh + (size_t)clampT(j + D - 1) * TILE_BYTES, rt0 + ((j + D - 1) % NBUF) * TILE_BYTES);
+    stage(Kh + (size_t)clampT(j + D) * TILE_BYTES, kt0 + ((j + D) % NBUF) * 2 * TILE_BYTES);
+    stage(Rh + (size_t)clampT(j + D - 1) * TILE_BYTES, rt0 + ((j + D - 1) % NBUF) * 2 * TILE_BYTES);
     mean_row(clampT(j + D - 1));
   };
   // the end of phase 2j+1: the copies of step j-1 and before (up to K tile j+2, R tile j+1)
@@ -194,10 +186,10 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     for (int i = t; i < MRING * 128 / 2; i += NWAVE * 64) ((uint32_t*)&mring[0][0])[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < D; ++i) stage(Kh + (size_t)clampT(i) * TILE_BYTES, kt0 + i * TILE_BYTES);
+  for (int i = 0; i < D; ++i) stage(Kh + (size_t)clampT(i) * TILE_BYTES, kt0 + i * 2 * TILE_BYTES);
 #pragma unroll
   for (int i = 0; i < D - 1; ++i) {
-    stage(Rh + (size_t)clampT(i) * TILE_BYTES, rt0 + i * TILE_BYTES);
+    stage(Rh + (size_t)clampT(i) * TILE_BYTES, rt0 + i * 2 * TILE_BYTES);
     mean_row(clampT(i));
   }
 
@@ -240,6 +232,17 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   wait_dma_barrier<0>();   // the first copies have landed
 
   const v8i ones = rowsum_ones(lane);
+  // byte offsets of this lane's 16-byte chunks 2hl, 2hl+1, 4+2hl, 5+2hl in row q of a tile (row
+  // 32 i + q adds 4096 i, an instruction offset), so a fragment address is one add
+  const uint32_t co0 = swz(q, 2 * hl), co1 = swz(q, 2 * hl + 1), co2 = swz(q, 4 + 2 * hl), co3 = swz(q, 5 + 2 * hl);
+  auto frag = [&](const uint8_t* t, uint32_t oa, uint32_t ob, int blk) {
+    const uint4 lo = *(const uint4*)(t + oa + 4096 * blk);
+    const uint4 hi = *(const uint4*)(t + ob + 4096 * blk);
+    v8i r;
+    r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    return r;
+  };
   float b = 0.0f, l_run = 0.0f;   // b = 119.65 - m; set on the first tile
   // b in every element: the QK accumulator input, kept in registers and rebuilt only when b
   // changes (a running-maximum update), not once per tile
@@ -325,11 +328,11 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     constexpr bool QK = decltype(qk)::value, PV = decltype(pv)::value;
     v8i kf[8];
     if constexpr (QK) {
-      const uint8_t* kb_ = kt[j % NBUF];
+      const uint8_t* kb_ = tiles[j % NBUF][0];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        kf[2 * kb] = lds_frag32(kb_, 32 * kb + q, 2 * hl);
-        kf[2 * kb + 1] = lds_frag32(kb_, 32 * kb + q, 4 + 2 * hl);
+        kf[2 * kb] = frag(kb_, co0, co1, kb);
+        kf[2 * kb + 1] = frag(kb_, co2, co3, kb);
       }
     }
     if constexpr (PV) {
@@ -447,11 +450,11 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     keep(pw[0]);
     keep(pw[1]);
     {   // the residual fragments of PV(j), the first products of M(j+1)
-      const uint8_t* rb = rt[j % NBUF];
+      const uint8_t* rb = tiles[j % NBUF][1];
 #pragma unroll
       for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int db = 0; db < 4; ++db) rf[4 * p + db] = lds_frag32(rb, 32 * db + q, 4 * p + 2 * hl);
+        for (int db = 0; db < 4; ++db) rf[4 * p + db] = frag(rb, p ? co2 : co0, p ? co3 : co1, db);
     }
     sa = e8m0_sk(j + 1 < T ? j + 1 : T - 1);   // for QK of tile j+1
     keep(sa);
