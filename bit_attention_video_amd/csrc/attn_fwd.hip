@@ -301,14 +301,19 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       for (int k = 0; k < 8; ++k) rB[k] = 0.0f;
     }
     snapped = false;
+    // rho = bf16 hi + bf16 lo, two values per hardware conversion (round to nearest even)
+    typedef float v2f_ __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf_ __attribute__((ext_vector_type(2)));
     v8s bhi, blo;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float rk = hl ? rA[k] : rB[k];
-      const uint32_t hi = f32_to_bf16_rne(rk);
-      bhi[k] = (short)hi;
-      blo[k] = (short)f32_to_bf16_rne(rk - bf16_to_f32(hi));
-      rA[k] = 0.0f;
+    for (int k = 0; k < 8; k += 2) {
+      const v2f_ x = {hl ? rA[k] : rB[k], hl ? rA[k + 1] : rB[k + 1]};
+      const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf_));
+      const v2f_ rest = {x[0] - __uint_as_float(hw << 16), x[1] - __uint_as_float(hw & 0xFFFF0000u)};
+      const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, v2bf_));
+      bhi[k] = (short)(hw & 0xFFFFu); bhi[k + 1] = (short)(hw >> 16);
+      blo[k] = (short)(lw & 0xFFFFu); blo[k + 1] = (short)(lw >> 16);
+      rA[k] = 0.0f; rA[k + 1] = 0.0f;
     }
     const int t0 = hl ? e - 7 : (e & ~15);   // tile of this lane's first K-slot
 #pragma unroll
