@@ -83,9 +83,12 @@ __device__ __forceinline__ int rowsum_ones4_word(int lane) {
   const bool one = (G & 1) ? (i == 4 || i == 12) : (i == 0 || i == 8);
   return one ? 0x22222222 : 0;   // eight E2M1 1.0
 }
-__device__ __forceinline__ v4i rowsum_ones4(int word) {
-  asm volatile("" : "+v"(word));
-  return v4i{word, word, word, word};
+// Built once and kept in registers for the whole key loop (opaque, so it is not rebuilt per tile).
+__device__ __forceinline__ v4i rowsum_ones4(int lane) {
+  const int word = rowsum_ones4_word(lane);
+  v4i r = v4i{word, word, word, word};
+  asm volatile("" : "+v"(r));
+  return r;
 }
 
 // E2M1 codes of 32 values x divided by their power-of-two group scale `scale`: nibble k = value
@@ -202,8 +205,11 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   }
   wait_dma_barrier<0>();
 
-  const int ones_word = rowsum_ones4_word(lane);
+  const v4i ones = rowsum_ones4(lane);
   float b = 0.0f, l_run = 0.0f;   // b = -m
+  // b in every element: the QK accumulator input, kept in registers and rebuilt only when b
+  // changes (a running-maximum update)
+  v16f bsplat = {};
   float rA[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) rA[k] = 0.0f;
@@ -251,14 +257,19 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
       for (int k = 0; k < 8; ++k) rB[k] = 0.0f;
     }
     snapped = false;
+    // rho = bf16 hi + bf16 lo, two values per hardware conversion (round to nearest even)
+    typedef float v2f_ __attribute__((ext_vector_type(2)));
+    typedef __bf16 v2bf_ __attribute__((ext_vector_type(2)));
     v8s bhi, blo;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float rk = hl ? rA[k] : rB[k];
-      const uint32_t hi = f32_to_bf16_rne(rk);
-      bhi[k] = (short)hi;
-      blo[k] = (short)f32_to_bf16_rne(rk - bf16_to_f32(hi));
-      rA[k] = 0.0f;
+    for (int k = 0; k < 8; k += 2) {
+      const v2f_ x = {hl ? rA[k] : rB[k], hl ? rA[k + 1] : rB[k + 1]};
+      const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf_));
+      const v2f_ rest = {x[0] - __uint_as_float(hw << 16), x[1] - __uint_as_float(hw & 0xFFFF0000u)};
+      const uint32_t lw = __builtin_bit_cast(uint32_t, __builtin_convertvector(rest, v2bf_));
+      bhi[k] = (short)(hw & 0xFFFFu); bhi[k + 1] = (short)(hw >> 16);
+      blo[k] = (short)(lw & 0xFFFFu); blo[k + 1] = (short)(lw >> 16);
+      rA[k] = 0.0f; rA[k + 1] = 0.0f;
     }
     const int t0 = hl ? e - 7 : (e & ~15);
 #pragma unroll
@@ -292,14 +303,10 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
         acc[db] = mfma_fp4<0, 0>(rf[db], pw[0], acc[db], rsw[db], psc);
         acc[db] = mfma_fp4<2, 1>(rf[4 + db], pw[1], acc[db], rsw[db], psc);
       }
-      const v4i ones = rowsum_ones4(ones_word);
       rs = mfma_fp4_16<0>(ones, pw[0], v4f{}, psc);
       rs = mfma_fp4_16<1>(ones, pw[1], rs, psc);
     }
     if constexpr (QK) {
-      v16f bsplat;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) bsplat[i] = b;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         s[kb] = mfma_fp4<0, 0>(kf[2 * kb], qf[0], bsplat, ksw[kb], qsc);
@@ -348,6 +355,14 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
           for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
       }
       b -= delta;
+      {   // eight 64-bit copies of the pair (b, b)
+        typedef double v8d __attribute__((ext_vector_type(8)));
+        double bb = __builtin_bit_cast(double, ((uint64_t)__float_as_uint(b) << 32) | __float_as_uint(b));
+        asm("" : "+v"(bb));   // opaque, so the compiler does not turn it back into a float splat
+        const v8d wv = {bb, bb, bb, bb, bb, bb, bb, bb};
+        bsplat = __builtin_bit_cast(v16f, wv);
+      }
+      asm volatile("" : "+v"(bsplat));   // opaque: kept, not rebuilt from b where it is used
     }
     // value k of PV step p is element (kb = 2p + k/16, i = k%16) of S^T
     int sc = 0;
