@@ -335,8 +335,9 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     if constexpr (QK) {
       const uint8_t* kb_ = tiles[j % NBUF][0];
 #pragma unroll
+      for (int kb = 0; kb < 4; ++kb) kf[2 * kb] = frag(kb_, co0, co1, kb);
+#pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        kf[2 * kb] = frag(kb_, co0, co1, kb);
         kf[2 * kb + 1] = frag(kb_, co2, co3, kb);
       }
     }
@@ -349,11 +350,12 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       rs = mfma_fp8_16(ones, pw[1], rs);
     }
     if constexpr (QK) {
+      // the first halves of the four chains, then the second halves: no product waits on the
+      // one issued just before it (the key fragments are read in that order too)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = mfma_fp8(kf[2 * kb], qf[0], bsplat, sa, sb);
-        s[kb] = mfma_fp8(kf[2 * kb + 1], qf[1], s[kb], sa, sb);
-      }
+      for (int kb = 0; kb < 4; ++kb) s[kb] = mfma_fp8(kf[2 * kb], qf[0], bsplat, sa, sb);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = mfma_fp8(kf[2 * kb + 1], qf[1], s[kb], sa, sb);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) keep(s[kb]);
     }
