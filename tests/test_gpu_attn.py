@@ -149,6 +149,26 @@ def test_attn_fwd_small_and_ragged_shapes():
                 assert T.rel_l2(O[b, h], ref) < TOL
 
 
+@pytest.mark.parametrize("N", [2048, 2176])
+def test_attn_fwd_mean_group_boundaries(N):
+    """The mean term's 16-tile groups at the key loop's end: N = 2048 (16 tiles: one full group,
+    closed after the loop) and N = 2176 (17 tiles: the full group closes in the last matrix phase,
+    then a one-tile group)."""
+    rng = np.random.default_rng(N)
+    note(f"mean-group boundary N={N}")
+    Q = F.bf16_bits_from_value(F.bf16_round(rng.standard_normal((1, 1, N, 128))))
+    K = F.bf16_bits_from_value(F.bf16_round(rng.standard_normal((1, 1, N, 128)) + 1.0))
+    V = F.bf16_bits_from_value(F.bf16_round(rng.standard_normal((1, 1, N, 128)) * 2 + 3.0))
+    perm = rng.permutation(N).astype(np.int32)[None, None]
+    O = vc.vc_attention(bf16_dev(Q), bf16_dev(K), bf16_dev(V), torch.from_numpy(perm).to(DEV), softmax_scale=0.05)
+    O = values(bf16_host_bits(O))[0, 0]
+    Qh, Kh, Vh = values(Q[0, 0]), values(K[0, 0]), values(V[0, 0])
+    ops = _oracle_ops(Qh, Kh, Vh, perm[0, 0], scale=0.05)
+    ref = T.attention_tiled(F.e4m3_decode(ops["qc"]), ops["sQ"], F.e4m3_decode(ops["kc"]), ops["sK"],
+                            F.e4m3_decode(ops["codes"]), ops["mu_t"], ops["sV"], scale=0.05)
+    assert T.rel_l2(O, ref) < TOL
+
+
 def test_attn_fwd_empty_is_noop():
     Q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV)
     Kq = torch.empty((1, 2, 0, 128), dtype=torch.uint8, device=DEV)
