@@ -145,7 +145,7 @@ def test_mx4_end_to_end_and_vsmooth_gain():
 
 
 def test_mx4_small_and_ragged_shapes():
-    for B, H, N in [(1, 1, 128), (2, 3, 384), (1, 2, 640)]:
+    for B, H, N in [(1, 1, 128), (2, 3, 384), (1, 2, 640), (1, 1, 2176)]:   # 2176 = 17 tiles: a full 16-tile mean group closes in the last matrix phase
         cfg, Q, K, V = config_inputs("medium", list(range(H)), B=B, N=N, grid=None, v_kind="iid")
         note(f"mx4 path B={B} H={H} N={N}")
         perm = np.stack([np.random.default_rng(b * H + h).permutation(N) for b in range(B) for h in range(H)])
