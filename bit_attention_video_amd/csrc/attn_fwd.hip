@@ -438,8 +438,11 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     }
     // ExpCast Round + clip: one saturating RNE byte conversion per element.  Byte jj of the
     // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
+    // key half 0's codes free the scores of key blocks 0-1, which then receive the residual
+    // fragments of PV half 0 while key half 1 is converted
+    const uint8_t* rb = tiles[j % NBUF][1];
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < 2; ++p) {
 #pragma unroll
       for (int wd = 0; wd < 8; ++wd) {
         const int kb = 2 * p + (wd >> 2), i0 = 4 * (wd & 3);
@@ -459,14 +462,10 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
         }
         pw[p][wd] = (int)word;
       }
-    keep(pw[0]);
-    keep(pw[1]);
-    {   // the residual fragments of PV(j), the first products of M(j+1)
-      const uint8_t* rb = tiles[j % NBUF][1];
+      keep(pw[p]);
+      // the residual fragments of PV(j) half p, the first products of M(j+1)
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) rf[4 * p + db] = frag(rb, p ? co2 : co0, p ? co3 : co1, db);
+      for (int db = 0; db < 4; ++db) rf[4 * p + db] = frag(rb, p ? co2 : co0, p ? co3 : co1, db);
     }
     sa = e8m0_sk(j + 1 < T ? j + 1 : T - 1);   // for QK of tile j+1
     keep(sa);
