@@ -19,15 +19,17 @@ __device__ __forceinline__ float pair_max(float x) {
 // is awaited explicitly (vmcnt) before the barrier that publishes a tile.
 // The global address is a per-lane 64-bit VGPR address.  (An SGPR base would need the five
 // wait states gfx9 requires between a vector write of an SGPR and a memory instruction that
-// reads it, which the compiler does not insert in front of inline assembly.)  The s_nop gives
-// the M0 write by the scalar unit a wait state before the copy reads it.
+// reads it, which the compiler does not insert in front of inline assembly.)  The compiler
+// writes M0 for the "{m0}" operand; the s_nop 4 in front of the copy gives five wait states,
+// enough for the strictest case (M0 written by a vector instruction such as v_readfirstlane;
+// a scalar write needs one), so the guard does not depend on how M0 was produced.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
   const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds_base) {
   const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
 }
 // Workgroup barrier between two phases.  No LDS read needs to be complete here: every tile
 // buffer is rewritten only after the instructions that consume its reads, and the compiler

@@ -162,6 +162,15 @@ def test_energy_identity_eq5():
     assert lhs == pytest.approx(e_r + 128 * ((c - mu) ** 2).sum(), rel=1e-12)
     assert e_r == pytest.approx(e_v - 128 * mu @ mu, rel=1e-12)
     assert 0.0 <= share <= 1.0
+    # with c = 0 the identity gives the mean's share of the block energy as 1 - ||R||^2 / ||V||^2
+    assert share == pytest.approx(1.0 - e_r / e_v, rel=1e-12)
+
+
+def test_diam2_closed_form():
+    # App. D Eq. 15: the largest distance between two rows (a 3-4-5 triangle, and a cube's diagonal)
+    assert A.diam2(np.array([[0.0, 0.0], [3.0, 4.0], [1.0, 1.0]])) == pytest.approx(5.0, rel=1e-15)
+    cube = np.array([[i, j, k] for i in (0, 1) for j in (0, 1) for k in (0, 1)], dtype=float)
+    assert A.diam2(cube) == pytest.approx(np.sqrt(3.0), rel=1e-15)
 
 
 def test_mean_storage_cost(golden):

@@ -170,3 +170,114 @@ def test_rotation_at_4_bits_on_channel_outliers():
     e_rot = _rows_err("qk_outlier", [0], True, "identity", hadamard=True)
     e_plain = _rows_err("qk_outlier", [0], True, "identity", hadamard=False)
     assert e_rot < e_plain
+
+
+def _brute_p4(P):
+    """Brute-force MX E2M1 quantiser of non-negative rows (rows, 128 keys): per (row, 32-key group
+    of key_group) the exponent is found by scanning E upwards for the first 6 * 2^E >= group max
+    (E >= -100; 0 for an all-zero group), then each element takes the nearest of the eight E2M1
+    magnitudes times 2^E, a tie going to the even code (the OCP MX E2M1 table)."""
+    out = np.empty_like(P)
+    grp = M.key_group(np.arange(P.shape[1]))
+    for r in range(P.shape[0]):
+        for g in range(4):
+            cols = np.nonzero(grp == g)[0]
+            amax = P[r, cols].max()
+            E = -100
+            if amax == 0:
+                E = 0
+            else:
+                while 6.0 * 2.0 ** E < amax:
+                    E += 1
+            for c in cols:
+                x = P[r, c] / 2.0 ** E
+                dist = [abs(x - v) for v in E2M1_TABLE]
+                best = min(dist)
+                cand = [i for i in range(8) if dist[i] == best]
+                i = cand[0] if len(cand) == 1 else [j for j in cand if j % 2 == 0][0]
+                out[r, c] = E2M1_TABLE[i] * 2.0 ** E
+    return out
+
+
+def test_quantize_p4_brute_force():
+    """oracle.mx4.quantize_p4 equals the brute-force per-(row, 32-key group) quantiser, including
+    exact ties, all-zero groups, tiny groups at the exponent floor and groups spanning many binades."""
+    rng = np.random.default_rng(30)
+    P = np.exp2(rng.uniform(-30, 0, (24, 128)))
+    P[0] = 0.0                                                     # all groups zero
+    P[1, :] = np.exp2(-140.0)                                      # below the exponent floor
+    P[2] = np.exp2(rng.uniform(-3, 0, 128))                        # narrow range
+    grp = M.key_group(np.arange(128))
+    for r in range(3, 9):                                          # exact midpoints between codes
+        for g in range(4):
+            cols = np.nonzero(grp == g)[0]
+            E = int(rng.integers(-20, 0))
+            k = rng.integers(0, 7, len(cols))
+            P[r, cols] = (np.array(E2M1_TABLE)[k] + np.array(E2M1_TABLE)[k + 1]) / 2 * 2.0 ** E
+            P[r, cols[0]] = 6.0 * 2.0 ** E                         # the group maximum sets E exactly
+    P[9, grp == 1] = 0.0                                           # one zero group in a live row
+    assert np.array_equal(M.quantize_p4(P), _brute_p4(P))
+
+
+def test_mx4_recurrence_closed_form():
+    """The tiled 4-bit recurrence (Eq. 1 with Eq. 6's mean term) against its closed form: with
+    m_j the running maximum after tile j and P_j the brute-force quantised 2^(S_j - m_j),
+    O = sum_j 2^(m_j - m_T) (P_j R_j + r_j mu_j) / sum_j 2^(m_j - m_T) r_j, r_j = P_j 1."""
+    rng = np.random.default_rng(31)
+    N, d, nq = 512, 128, 6
+    Qv = rng.standard_normal((nq, d)) * 0.4
+    Kv = rng.standard_normal((N, d))
+    Kv[300] *= 4.0                                                 # moves the running maximum late
+    Rv = rng.standard_normal((N, d))
+    mu = rng.standard_normal((N // 128, d)) * 3
+    O = M.attention_tiled_mx4(Qv, Kv, Rv, mu, p_mode="mx4", round_output=False)
+    m = -np.inf
+    terms = []
+    for j in range(N // 128):
+        s = F.fl32(Qv @ Kv[128 * j:128 * (j + 1)].T).astype(np.float64)
+        m = np.maximum(m, s.max(1))
+        P = _brute_p4(F.fl32(np.exp2(F.fl32(s - m[:, None]).astype(np.float64))).astype(np.float64))
+        terms.append((m.copy(), P @ Rv[128 * j:128 * (j + 1)] + P.sum(1)[:, None] * mu[j][None, :], P.sum(1)))
+    mT = terms[-1][0]
+    num = sum(np.exp2(mj - mT)[:, None] * a for mj, a, _ in terms)
+    den = sum(np.exp2(mj - mT) * r for mj, _, r in terms)
+    assert np.allclose(O, num / den[:, None], rtol=1e-12, atol=0)
+
+
+def test_q4_k4_quantisers_fold_slope_and_centre():
+    """The 4-bit Q path multiplies by L4 = fl32(log2(e)/sqrt(d)) before its per-32-channel
+    quantiser, and the K path centres by the key channel mean and gathers by pi: each dequantised
+    element lies within half an E2M1 step (at most the group scale, the half step of the 4..6
+    binade) of fl32(Q) L4, resp. K[pi] - kbar."""
+    rng = np.random.default_rng(32)
+    N = 256
+    Q = F.bf16_round(rng.standard_normal((N, 128)))
+    K = F.bf16_round(rng.standard_normal((N, 128)) + 2.0 * rng.standard_normal(128))
+    perm = rng.permutation(N)
+    qc, qE = M.quantize_q4(Q)
+    X = F.fl32(Q).astype(np.float64) * float(np.float32(np.log2(np.e) / np.sqrt(128)))
+    sc = np.repeat(np.ldexp(1.0, qE), 32, axis=1)
+    assert np.all(np.abs(M.dequant_row_groups(qc, qE) - X) <= sc + 1e-6 * np.abs(X))
+    kc, kE = M.quantize_k4(K, perm)
+    Kc = F.fl32(K[perm]).astype(np.float64) - S.key_channel_mean(K).astype(np.float64)[None, :]
+    sc = np.repeat(np.ldexp(1.0, kE), 32, axis=1)
+    assert np.all(np.abs(M.dequant_row_groups(kc, kE) - Kc) <= sc + 1e-6 * np.abs(Kc))
+    assert np.abs(Kc.mean(0)).max() < 1e-5
+
+
+def test_k4_rotated_keys_are_the_centred_keys_times_h_over_d():
+    """With the QK rotation the 4-bit K path quantises fl32((K[pi] - kbar) H) per 32-channel group
+    and stores its exponent lowered by 7, so the dequantised keys are (K[pi] - kbar) H / 128 = the
+    centred keys times H^-T, within half an E2M1 step of the stored group scale (at most the
+    scale)."""
+    from oracle import rotation as R
+    rng = np.random.default_rng(33)
+    N = 256
+    K = F.bf16_round(rng.standard_normal((N, 128)) + 2.0 * rng.standard_normal(128))
+    perm = rng.permutation(N)
+    kc, kE = M.quantize_k4(K, perm, hadamard=True)
+    Kc = (F.fl32(K[perm]) - S.key_channel_mean(K)[None, :]).astype(np.float32)
+    want = R.rotate(Kc).astype(np.float64) / 128.0
+    sc = np.repeat(np.ldexp(1.0, kE), 32, axis=1)
+    assert np.all(np.abs(M.dequant_row_groups(kc, kE) - want) <= sc)
+    assert np.all(np.abs(want).reshape(N, 4, 32).max(2) > 3.0 * np.ldexp(1.0, kE))   # the smallest scale

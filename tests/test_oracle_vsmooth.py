@@ -177,3 +177,36 @@ def test_q_quantiser_folds_log2e_scale():
     assert np.all(np.abs(deq - Qs) <= np.abs(Qs) * 2.0 ** -4 + np.repeat(sQ, 128)[:, None] * 2.0 ** -10)
     codes2, sQ2 = S.quantize_q(Q, softmax_scale=0.5)
     assert not np.array_equal(sQ2, sQ) or not np.array_equal(codes2, codes)
+
+
+def test_quantize_v_zero_residual_and_constant_block():
+    """Reading of the V scale for a channel with no residual (Sec. 3.2 Eq. 4; App. B): a channel
+    that is constant inside every 128-row block has R = 0, so amax = 0 and s_V = 1, its codes are
+    zero and its stored mean is bf16(mu) itself; a block constant in every channel contributes
+    zero residual codes while the other blocks keep theirs."""
+    rng = np.random.default_rng(12)
+    N, d = 384, 128
+    V = F.bf16_round(rng.standard_normal((N, d)))
+    V[:, 5] = np.repeat(F.bf16_round(rng.standard_normal(3) * 4), 128)      # block-constant channel
+    V[128:256] = F.bf16_round(rng.standard_normal(d))[None, :]            # constant block
+    q = S.quantize_v(V, np.arange(N))
+    assert q["sV"][5] == 1.0
+    assert np.all(q["codes"][:, 5] == 0)
+    assert np.array_equal(q["mu_t"][:, 5], F.bf16_round(V[::128, 5]))
+    assert np.all((q["codes"][128:256] & 0x7F) == 0)
+    assert np.any(q["codes"][:128] != 0) and np.any(q["codes"][256:] != 0)
+    # per-channel scale is the residual's amax / 448 elsewhere (the E4M3 maximum is reached)
+    live = np.arange(d) != 5
+    assert np.all(np.abs(F.e4m3_decode(q["codes"][:, live])).max(0) == 448.0)
+
+
+def test_key_channel_mean_closed_form():
+    """The key channel mean (Sec. 2; App. B's centering statistics) of a matrix whose columns are
+    known arithmetic sequences, and the centred rows' column sums."""
+    N = 1024
+    t = np.arange(N, dtype=np.float64)
+    K = np.stack([t * 2.0 ** -6, -t * 2.0 ** -8 + 3.0, np.full(N, 7.25)] + [np.zeros(N)] * 125, axis=1)
+    kbar = S.key_channel_mean(K)
+    assert kbar[0] == np.float32((N - 1) / 2 * 2.0 ** -6)
+    assert kbar[1] == np.float32(3.0 - (N - 1) / 2 * 2.0 ** -8)
+    assert kbar[2] == np.float32(7.25) and np.all(kbar[3:] == 0)
