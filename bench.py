@@ -94,6 +94,63 @@ def measured_fp8_peak(vc, torch, workgroups=4096, iters=2000):
     return workgroups * iters * 4194304.0 / (best * 1e-3) / 1e12, clock
 
 
+def attn_clock_probe(vc, torch, Qd, ops, O, reps=5):
+    """The attention kernel with its clock stamps on (vc_test_attn_fwd_clock), `reps` launches
+    back to back timed with HIP events on the launch stream.  Returns (ms per launch, the shader
+    clock in GHz the last launch ran at: its workgroups' summed shader cycles over their summed
+    constant-rate ticks, times the counter's rate)."""
+    args = (Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"])
+    _, clk = vc.vc_test_attn_fwd_clock(*args, out=O)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        vc.vc_test_attn_fwd_clock(*args, out=O, clk=clk)
+    e1.record()
+    torch.cuda.synchronize()
+    c = clk.cpu().numpy().astype(np.float64)
+    ghz = (c[:, 2] - c[:, 0]).sum() / (c[:, 3] - c[:, 1]).sum() * vc.wall_clock_mhz() * 1e-3
+    return e0.elapsed_time(e1) / reps, float(ghz)
+
+
+def accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads, nrows=256):
+    """Accuracy of the timed path on sampled heads (computed after the timed region): the GPU output
+    against the oracle's emulated recurrence on the GPU's permutation and against FP64 exact
+    attention; the two unsmoothed sequence-order baselines (same P path, and exp-then-cast P)
+    against exact; the grouping objective against the oracle's Lloyd from the same start."""
+    from oracle import attention as T
+    from oracle import formats as F
+    from oracle import vsmooth as S
+    import torch
+    perm = g["perm"].cpu().numpy()
+    J = g["J"].cpu().numpy()
+    val = lambda t: F.bf16_value_from_bits(t.cpu().view(torch.int16).numpy().view(np.uint16))
+    O, Ob, Oe = val(O), val(Ob), val(Oe)
+    rows = np.unique(np.linspace(0, cfg.N - 1, nrows).round().astype(np.int64))
+    r = {"emu": [], "vc": [], "base": [], "etc": [], "J": []}
+    for h in heads:
+        Qh, Kh, Vh = (F.bf16_value_from_bits(x[0, h]) for x in (Q, K, V))
+        qc, sQ = S.quantize_q(Qh)
+        kc, sK = S.quantize_k(Kh, perm[0, h])
+        vq = S.quantize_v(Vh, perm[0, h])
+        emu = T.attention_tiled(F.e4m3_decode(qc), sQ, F.e4m3_decode(kc), sK, F.e4m3_decode(vq["codes"]),
+                                vq["mu_t"], vq["sV"], rows=rows)
+        exact = T.attention_exact(Qh, Kh, Vh, rows=rows)
+        r["emu"].append(T.rel_l2(O[0, h][rows], emu))
+        r["vc"].append(T.rel_l2(O[0, h][rows], exact))
+        r["base"].append(T.rel_l2(Ob[0, h][rows], exact))
+        r["etc"].append(T.rel_l2(Oe[0, h][rows], exact))
+        J_ref = S.vsmooth_group(Vh, cfg.k, cfg.iters)["J"]
+        r["J"].append(abs(float(J[0, h]) - J_ref) / J_ref)
+    mean = lambda k: float(np.mean(r[k]))
+    return {"heads": list(heads), "rows_per_head": int(len(rows)),
+            "rel_l2_vs_emulated_max": round(max(r["emu"]), 6), "tolerance_vs_emulated": 5e-3,
+            "rel_l2_vs_exact": round(mean("vc"), 6),
+            "unsmoothed_same_p_vs_exact": round(mean("base"), 6),
+            "unsmoothed_exp_then_cast_vs_exact": round(mean("etc"), 6),
+            "vc_below_unsmoothed": mean("vc") < mean("base"),
+            "kmeans_J_rel_err_max": float(f"{max(r['J']):.3e}")}
+
+
 def reuse_schedule(args, cfg, vc, torch):
     """The permutation-reuse workload: V drifts over cfg.steps steps; grouping runs on the
     first step only and pi is reused (the pages' amortisation, Sec. 3.4).  Also times a
@@ -185,6 +242,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="video")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-accuracy", action="store_true", help="skip the oracle accuracy report")
     ap.add_argument("--attn-only-iters", type=int, default=0,
                     help="extra back-to-back vc_attn_fwd launches timed alone (for profiling)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -332,6 +390,8 @@ def main():
         proto.append(e0.elapsed_time(e1))
     t_attn_med = float(np.median(proto))
     log(f"attention alone, median of 50 after 20 warm-up launches: {t_attn_med:.3f} ms")
+    probe_ms, kernel_ghz = attn_clock_probe(vc, torch, Qd, ops, O)
+    log(f"attention clock probe: {probe_ms:.3f} ms per launch at a {kernel_ghz:.3f} GHz shader clock")
     fp8_peak_meas, clock_ghz = measured_fp8_peak(vc, torch)
     log(f"measured dense FP8 rate {fp8_peak_meas:.0f} TFLOP/s at a {clock_ghz:.2f} GHz shader clock "
         f"(vendor figure {FP8_PEAK_TFLOPS:.0f})")
@@ -362,7 +422,10 @@ def main():
                      "kernel": "k_attn_fwd", "avg_launch_ms": round(t_attn, 4),
                      "measured_peak": round(fp8_peak_meas, 1),
                      "measured_peak_clock_ghz": round(clock_ghz, 3),
-                     "frac_of_measured_peak": round(attn_tflops / fp8_peak_meas, 4)},
+                     "frac_of_measured_peak": round(attn_tflops / fp8_peak_meas, 4),
+                     "kernel_clock_ghz": round(kernel_ghz, 3), "clock_probe_ms": round(probe_ms, 4),
+                     "clock_probe_frac": round(fl / (probe_ms * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4),
+                     "frac_of_clock_peak": round(fl / (probe_ms * 1e-3) / (256 * 8192 * kernel_ghz * 1e9), 4)},
         "attn_protocol": {"warmup_launches": 20, "launches": 50, "median_ms": round(t_attn_med, 4),
                           "tflops": round(fl / (t_attn_med * 1e-3) / 1e12, 2),
                           "frac": round(fl / (t_attn_med * 1e-3) / 1e12 / FP8_PEAK_TFLOPS, 4)},
@@ -380,6 +443,16 @@ def main():
                         "attn_over_unrotated": round(t_attn_rot / t_attn, 4),
                         "demean_quant_over_unrotated": round(t_dq_rot / t_dq, 4)},
     }
+    if not args.no_accuracy:
+        log("accuracy on sampled heads (oracle, outside the timed region)")
+        base = vc.vc_vsmooth_demean_quant(Kd, Vd, None, no_demean=True)
+        bargs = (Qd, base["Kq"], base["sK"], base["Rq"], None, base["sV"])
+        Ob = vc.vc_attn_fwd(*bargs, no_mean=True)
+        Oe = vc.vc_attn_fwd(*bargs, no_mean=True, exp_then_cast=True)
+        O = vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"])
+        out["accuracy"] = accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads=sorted({0, H // 2, H - 1}))
+        del base, Ob, Oe
+        log(f"accuracy: {json.dumps(out['accuracy'])}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         perm0 = np.random.default_rng(0).permutation(N)   # any permutation: the cost does not depend on it

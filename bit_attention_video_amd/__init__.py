@@ -27,7 +27,9 @@ __all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_
            "vc_test_fp4_encode", "vc_test_mfma_fp8_rate", "unpack_fp4", "pack_fp4", "vc_test_expcast", "vc_test_e4m3_encode", "vc_test_kmeans_assign",
            "vc_test_label_sort", "rq_tiled_to_natural", "rq_natural_to_tiled", "LIB_PATH",
            "VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_ATTN_HADAMARD", "VC_DQ_NO_DEMEAN",
-           "VC_DQ_HADAMARD", "STATUS"]
+           "VC_DQ_HADAMARD", "STATUS", "vc_workspace_size", "vc_validate_perm", "vc_test_quantize_q",
+           "vc_test_attn_fwd_clock", "VC_OP_GROUP", "VC_OP_DEMEAN_QUANT", "VC_OP_DEMEAN_QUANT_MX4",
+           "VC_OP_ATTN_FWD", "VC_OP_ATTN_FWD_MX4", "VC_OP_VALIDATE_PERM", "wall_clock_mhz"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvcattn.so")
 
@@ -36,6 +38,12 @@ VC_ATTN_EXP_THEN_CAST = 0x2
 VC_ATTN_HADAMARD = 0x4
 VC_DQ_NO_DEMEAN = 0x1
 VC_DQ_HADAMARD = 0x2
+VC_OP_GROUP = 1
+VC_OP_DEMEAN_QUANT = 2
+VC_OP_DEMEAN_QUANT_MX4 = 3
+VC_OP_ATTN_FWD = 4
+VC_OP_ATTN_FWD_MX4 = 5
+VC_OP_VALIDATE_PERM = 6
 STATUS = {"VC_OK": 0, "VC_ERR_NULL": -1, "VC_ERR_SHAPE": -2, "VC_ERR_K": -3, "VC_ERR_ITERS": -4,
           "VC_ERR_WORKSPACE": -5, "VC_ERR_OVERFLOW": -6, "VC_ERR_FLAGS": -7, "VC_ERR_HIP": -8}
 
@@ -61,6 +69,12 @@ _SIGNATURES = {
     "vc_test_e4m3_encode": (_I, [_P, _P, _Z, _P]),
     "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "vc_test_label_sort": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
+    "vc_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "vc_validate_perm": (_I, [_P, _I, _I, _I, _P, _P, _Z, _P]),
+    "vc_test_quantize_q": (_I, [_P, _I, _I, _I, _I, _F, _U, _P, _P, _P]),
+    "vc_test_attn_clock_slots": (_Z, [_I, _I, _I]),
+    "vc_test_wall_clock_khz": (_I, [ctypes.POINTER(_I)]),
+    "vc_test_attn_fwd_clock": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P, _P]),
 }
 
 _lib = None
@@ -201,6 +215,65 @@ def vc_attention(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool
     ops = vc_vsmooth_demean_quant(K, V, perm, no_demean=no_demean, hadamard=hadamard)
     return vc_attn_fwd(Q, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"], softmax_scale,
                        no_mean=no_demean, hadamard=hadamard)
+
+
+def vc_workspace_size(op: int, B: int, H: int, N: int, d: int = 128, k: int = 1) -> int:
+    """Scratch bytes the call `op` (VC_OP_*) needs for this shape."""
+    return int(lib().vc_workspace_size(op, B, H, N, d, k))
+
+
+def vc_validate_perm(perm: torch.Tensor) -> torch.Tensor:
+    """Per (b, h): entries of pi outside [0, N) plus repeats (0 = a permutation), as int32 [B, H]."""
+    if perm.dim() != 3:
+        raise ValueError("perm must be [B, H, N]")
+    _need(perm, "perm", torch.int32)
+    B, H, N = perm.shape
+    bad = torch.empty((B, H), dtype=torch.int32, device=perm.device)
+    nws = vc_workspace_size(VC_OP_VALIDATE_PERM, B, H, N)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=perm.device)
+    _check(lib().vc_validate_perm(_ptr(perm), B, H, N, _ptr(bad), _ptr(ws), nws, _stream()), "vc_validate_perm")
+    return bad
+
+
+def vc_test_quantize_q(Q: torch.Tensor, softmax_scale: float = 0.0, hadamard: bool = False):
+    """The attention kernel's query prologue alone: (E4M3 codes [B,H,N,d], block scales [B,H,N/128])."""
+    B, H, N, d = _bhnd(Q, "Q")
+    Qq = torch.empty((B, H, N, d), dtype=torch.uint8, device=Q.device)
+    sQ = torch.empty((B, H, N // 128 if N % 128 == 0 else 0), dtype=torch.float32, device=Q.device)
+    _check(lib().vc_test_quantize_q(_ptr(Q), B, H, N, d, float(softmax_scale), VC_ATTN_HADAMARD if hadamard else 0,
+                                    _ptr(Qq), _ptr(sQ), _stream()), "vc_test_quantize_q")
+    return Qq, sQ
+
+
+def vc_test_attn_fwd_clock(Q, Kq, sK, Rq, mu, sV, softmax_scale: float = 0.0, no_mean: bool = False,
+                           out: Optional[torch.Tensor] = None, clk: Optional[torch.Tensor] = None):
+    """vc_attn_fwd's kernel with its clock stamps on.  Returns (O, clk) with clk int64
+    [workgroups, 4] = (start cycles, start ticks, end cycles, end ticks) per workgroup."""
+    B, H, N, d = _bhnd(Q, "Q")
+    T = N // 128 if N % 128 == 0 else 0
+    _need(Kq, "Kq", torch.uint8, (B, H, N, d))
+    _need(sK, "sK", torch.float32, (B, H, T))
+    _need(Rq, "Rq", torch.uint8, (B, H, T, d, 128))
+    if mu is not None or not no_mean:
+        _need(mu, "mu", torch.bfloat16, (B, H, T, d))
+    _need(sV, "sV", torch.float32, (B, H, d))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=Q.device)
+    n = int(lib().vc_test_attn_clock_slots(B, H, N))
+    if clk is None:
+        clk = torch.zeros((max(n, 4) // 4, 4), dtype=torch.int64, device=Q.device)
+    _need(clk, "clk", torch.int64, (n // 4, 4))
+    _check(lib().vc_test_attn_fwd_clock(_ptr(Q), _ptr(Kq), _ptr(sK), _ptr(Rq), _ptr(mu), _ptr(sV), B, H, N, d,
+                                        float(softmax_scale), VC_ATTN_NO_MEAN if no_mean else 0, _ptr(out),
+                                        _ptr(clk), _stream()), "vc_test_attn_fwd_clock")
+    return out, clk
+
+
+def wall_clock_mhz() -> float:
+    """Frequency of the device's constant-rate counter (the clock probe's time base), in MHz."""
+    khz = _I(0)
+    _check(lib().vc_test_wall_clock_khz(ctypes.byref(khz)), "vc_test_wall_clock_khz")
+    return khz.value * 1e-3
 
 
 def vc_vsmooth_demean_quant_mx4(K: torch.Tensor, V: torch.Tensor, perm: Optional[torch.Tensor] = None,

@@ -31,6 +31,8 @@ int check_shape(int B, int H, int N, int d) {
 
 }  // namespace
 
+int vc_hip_status(hipError_t e) { return hip_status(e); }
+
 vc_group_ws vc_group_ws_layout(int BH, int N, int k) {
   vc_group_ws L;
   size_t nblk = (size_t)(N + VC_SORT_TILE - 1) / VC_SORT_TILE;
@@ -158,7 +160,73 @@ int vc_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uin
   // L = float32(8 log2(e) * scale), the scale taken in double (1/sqrt(d) when 0 is passed)
   const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;
   const float L = (float)(8.0 * 1.4426950408889634 * scale);
-  return hip_status(vc_launch_attn_fwd(Q, Kq, sK, Rq, mu, sV, B * H, N, L, flags, O, stream));
+  return hip_status(vc_launch_attn_fwd(Q, Kq, sK, Rq, mu, sV, B * H, N, L, flags, O, nullptr, stream));
+}
+
+size_t vc_workspace_size(int op, int B, int H, int N, int d, int k) {
+  if (d != VC_HEAD_DIM) return 0;
+  switch (op) {
+    case VC_OP_GROUP: return vc_group_workspace_size(B, H, N, k);
+    case VC_OP_DEMEAN_QUANT:
+    case VC_OP_DEMEAN_QUANT_MX4: return vc_demean_quant_workspace_size(B, H, N);
+    case VC_OP_VALIDATE_PERM:
+      if (B <= 0 || H <= 0 || N <= 0) return 0;
+      return align256((size_t)B * H * (size_t)((N + 31) / 32) * sizeof(uint32_t));
+    case VC_OP_ATTN_FWD:
+    case VC_OP_ATTN_FWD_MX4: return 0;
+    default: return 0;
+  }
+}
+
+int vc_validate_perm(const int32_t* perm, int B, int H, int N, int32_t* bad, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return VC_ERR_SHAPE;
+  if (B == 0 || H == 0 || N == 0) return VC_OK;
+  if ((long long)B * H * (long long)N >= (1LL << 31)) return VC_ERR_OVERFLOW;
+  if (!perm || !bad || !ws) return VC_ERR_NULL;
+  if (ws_bytes < vc_workspace_size(VC_OP_VALIDATE_PERM, B, H, N, VC_HEAD_DIM, 1)) return VC_ERR_WORKSPACE;
+  return hip_status(vc_launch_validate_perm(perm, B * H, N, (uint32_t*)ws, bad, stream));
+}
+
+int vc_test_quantize_q(const uint16_t* Q, int B, int H, int N, int d, float softmax_scale, unsigned flags,
+                       uint8_t* Qq, float* sQ, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!Q || !Qq || !sQ) return VC_ERR_NULL;
+  if (flags & ~VC_ATTN_HADAMARD) return VC_ERR_FLAGS;
+  if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return VC_ERR_SHAPE;
+  const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;
+  const float L = (float)(8.0 * 1.4426950408889634 * scale);
+  return hip_status(vc_launch_test_qquant(Q, B * H, N, L, (flags & VC_ATTN_HADAMARD) != 0, Qq, sQ, stream));
+}
+
+int vc_test_wall_clock_khz(int* khz) {
+  if (!khz) return VC_ERR_NULL;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(khz, hipDeviceAttributeWallClockRate, dev);
+  return hip_status(e);
+}
+
+size_t vc_test_attn_clock_slots(int B, int H, int N) {
+  if (B <= 0 || H <= 0 || N <= 0 || N % VC_BLOCK) return 0;
+  return 4 * (size_t)vc_attn_fwd_workgroups(B * H, N);
+}
+
+int vc_test_attn_fwd_clock(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uint8_t* Rq,
+                           const uint16_t* mu, const float* sV, int B, int H, int N, int d,
+                           float softmax_scale, unsigned flags, uint16_t* O, uint64_t* clk, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!Q || !Kq || !sK || !Rq || !sV || !O || !clk) return VC_ERR_NULL;
+  if (!mu && !(flags & VC_ATTN_NO_MEAN)) return VC_ERR_NULL;
+  if (flags & ~(VC_ATTN_NO_MEAN | VC_ATTN_EXP_THEN_CAST | VC_ATTN_HADAMARD)) return VC_ERR_FLAGS;
+  if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return VC_ERR_SHAPE;
+  const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;
+  const float L = (float)(8.0 * 1.4426950408889634 * scale);
+  return hip_status(vc_launch_attn_fwd(Q, Kq, sK, Rq, mu, sV, B * H, N, L, flags, O, clk, stream));
 }
 
 int vc_vsmooth_demean_quant_mx4(const uint16_t* K, const uint16_t* V, const int32_t* perm,

@@ -121,4 +121,54 @@ __device__ __forceinline__ void hadamard_q_row(float* x, int hl) {
   }
 }
 
+// Query prologue of the 8-bit attention (App. B's Q pass): lane (q, hl) of a wave owns query
+// row q and holds its channels 64 c + 32 hl + 8 m + j as x[32 c + 8 m + j] (c, hl in {0,1},
+// m < 4, j < 8), multiplied by L = float32(8 log2(e) softmax_scale), then rotated by H when HAD.
+template <bool HAD>
+__device__ __forceinline__ void q_row_scaled(const uint16_t* __restrict__ qrow, int hl, float L, float* x) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint4 raw = *(const uint4*)(qrow + 64 * c + 32 * hl + 8 * m);
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[32 * c + 8 * m + 2 * e] = bf16_to_f32(wd[e] & 0xFFFFu) * L;
+        x[32 * c + 8 * m + 2 * e + 1] = bf16_to_f32(wd[e] >> 16) * L;
+      }
+    }
+  if constexpr (HAD) hadamard_q_row(x, hl);
+}
+__device__ __forceinline__ float q_row_absmax(const float* x) {
+  float a = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 64; ++k) a = fmaxf(a, fabsf(x[k]));
+  return a;
+}
+// E4M3 codes of x / 2^EQ (qinv = 2^-EQ, exact): word d4 of qf[c] holds the codes of channels
+// 64 c + 32 hl + 4 d4 .. 64 c + 32 hl + 4 d4 + 3, the A/B operand bytes of the QK product.
+__device__ __forceinline__ void q_row_codes(const float* x, float qinv, v8i* qf) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int d4 = 0; d4 < 8; ++d4) {
+      const float* y = &x[32 * c + 4 * d4];
+      qf[c][d4] = (int)e4m3x4(y[0] * qinv, y[1] * qinv, y[2] * qinv, y[3] * qinv);
+    }
+}
+
+// Shader-clock stamp: the shader-cycle counter (s_memtime) and the constant-rate counter
+// (s_memrealtime) written by lane 0 of the calling wave to out[0], out[1].  A workgroup writes one stamp
+// at its start and one at its end; nothing stays live in registers in between.
+__device__ __forceinline__ void clock_stamp(uint64_t* out) {
+  if (out) {
+    const uint64_t w = wall_clock64(), c = clock64();
+    if (__lane_id() == 0) {
+      out[0] = c;
+      out[1] = w;
+    }
+  }
+}
+
 }  // namespace vc_attn

@@ -128,7 +128,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
                                                   const uint8_t* __restrict__ Rq,
                                                   const uint16_t* __restrict__ mu,
                                                   const float* __restrict__ sV, int N, int nqb,
-                                                  int nwb, uint32_t G, float L, uint16_t* __restrict__ O) {
+                                                  int nwb, uint32_t G, float L, uint16_t* __restrict__ O,
+                                                  uint64_t* __restrict__ clk) {
   // ring slot s holds K tile at tiles[s][0] and R tile at tiles[s][1]: one slot base serves both
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[NBUF][2][TILE_BYTES];
   __shared__ __attribute__((aligned(256))) uint16_t mring[MRING][128];
@@ -139,6 +140,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   const int t = threadIdx.x, lane = t & 63, q = lane & 31, hl = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6);
   const int grp = w >> 2;
+  // the clock probe (clk non-null): wave 0 stamps the workgroup's start and end
+  if (w == 0) clock_stamp(clk ? clk + 4 * blockIdx.x : nullptr);
   const uint32_t item = xcd_remap(blockIdx.x, G);
   const int bh = (int)(item / (uint32_t)nwb), qb = 2 * (int)(item % (uint32_t)nwb) + grp;
   const bool valid = qb < nqb;   // the last block of a head may have no second query block
@@ -198,38 +201,16 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   // 128 x 128 block), E4M3 ----
   const uint16_t* qrow = Q + (headN + qi) * VC_D;
   float qs[64];
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint4 raw = *(const uint4*)(qrow + 64 * c + 32 * hl + 8 * m);
-      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qs[32 * c + 8 * m + 2 * e] = bf16_to_f32(wd[e] & 0xFFFFu) * L;
-        qs[32 * c + 8 * m + 2 * e + 1] = bf16_to_f32(wd[e] >> 16) * L;
-      }
-    }
-  if constexpr (HAD) hadamard_q_row(qs, hl);
-  float amax = 0.0f;
-#pragma unroll
-  for (int k = 0; k < 64; ++k) amax = fmaxf(amax, fabsf(qs[k]));
-  amax = wave_max(amax);
+  q_row_scaled<HAD>(qrow, hl, L, qs);
+  float amax = wave_max(q_row_absmax(qs));
   if (lane == 0) red[w] = amax;
   __syncthreads();   // red[] and the cleared ring
   const int r0 = 4 * grp;
   amax = fmaxf(fmaxf(red[r0], red[r0 + 1]), fmaxf(red[r0 + 2], red[r0 + 3]));
   const int EQ = pow2_block_exponent(amax);
   const int sb = 127 + EQ;                         // E8M0 of sQ
-  const float qinv = __builtin_ldexpf(1.0f, -EQ);  // exact
   v8i qf[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int d4 = 0; d4 < 8; ++d4) {
-      const float* x = &qs[32 * c + 4 * d4];
-      qf[c][d4] = (int)e4m3x4(x[0] * qinv, x[1] * qinv, x[2] * qinv, x[3] * qinv);
-    }
+  q_row_codes(qs, __builtin_ldexpf(1.0f, -EQ), qf);
   wait_dma_barrier<0>();   // the first copies have landed
 
   const v8i ones = rowsum_ones(lane);
@@ -546,16 +527,55 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       const uint32_t o3 = f32_to_bf16_rne(acc[db][4 * ig + 3] * s4.w * inv_l);
       *(uint2*)(orow + d0) = make_uint2(o0 | (o1 << 16), o2 | (o3 << 16));
     }
+  if (w == 0) clock_stamp(clk ? clk + 4 * blockIdx.x + 2 : nullptr);
+}
+
+// The query prologue of k_attn_fwd on its own: one workgroup of four waves per 128-row block,
+// each wave 32 rows in the kernel's lane layout, the same helpers; writes the E4M3 codes in
+// natural layout Qq [BH][N][128] and the block scales sQ [BH][N/128] (2^EQ).
+template <bool HAD>
+__global__ __launch_bounds__(256) void k_test_qquant(const uint16_t* __restrict__ Q, int N, float L,
+                                                     uint8_t* __restrict__ Qq, float* __restrict__ sQ) {
+  __shared__ float red[4];
+  const int t = threadIdx.x, lane = t & 63, q = lane & 31, hl = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const size_t row = (size_t)blockIdx.y * N + (size_t)blockIdx.x * 128 + 32 * w + q;
+  float qs[64];
+  q_row_scaled<HAD>(Q + row * VC_D, hl, L, qs);
+  float amax = wave_max(q_row_absmax(qs));
+  if (lane == 0) red[w] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int EQ = pow2_block_exponent(amax);
+  v8i qf[2];
+  q_row_codes(qs, __builtin_ldexpf(1.0f, -EQ), qf);
+  uint8_t* out = Qq + row * VC_D;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int d4 = 0; d4 < 8; ++d4) *(int*)(out + 64 * c + 32 * hl + 4 * d4) = qf[c][d4];
+  if (t == 0) sQ[(size_t)blockIdx.y * (N / 128) + blockIdx.x] = __builtin_ldexpf(1.0f, EQ);
+}
+
+uint32_t vc_attn_fwd_workgroups(int BH, int N) { return (uint32_t)BH * (uint32_t)((N / 128 + 1) / 2); }
+
+hipError_t vc_launch_test_qquant(const uint16_t* Q, int BH, int N, float L, bool hadamard, uint8_t* Qq, float* sQ,
+                                 hipStream_t s) {
+  if (hadamard)
+    hipLaunchKernelGGL(k_test_qquant<true>, dim3(N / 128, BH), dim3(256), 0, s, Q, N, L, Qq, sQ);
+  else
+    hipLaunchKernelGGL(k_test_qquant<false>, dim3(N / 128, BH), dim3(256), 0, s, Q, N, L, Qq, sQ);
+  return hipGetLastError();
 }
 
 hipError_t vc_launch_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK,
                               const uint8_t* Rq, const uint16_t* mu, const float* sV,
                               int BH, int N, float L, unsigned flags, uint16_t* O,
-                              hipStream_t s) {
+                              uint64_t* clk, hipStream_t s) {
   const int nqb = N / 128, nwb = (nqb + 1) / 2;
-  const uint32_t G = (uint32_t)BH * (uint32_t)nwb;
+  const uint32_t G = vc_attn_fwd_workgroups(BH, N);
   auto launch = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb, G, L, O);
+    hipLaunchKernelGGL(kern, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq, sK, Rq, mu, sV, N, nqb, nwb, G, L, O, clk);
   };
   const bool no_mean = flags & VC_ATTN_NO_MEAN, etc = flags & VC_ATTN_EXP_THEN_CAST;
   if (flags & VC_ATTN_HADAMARD) {

@@ -22,8 +22,12 @@
 #include "vc_internal.h"
 #include "vc_attn.h"
 
+// Token at permuted position pos.  An entry outside [0, N) (a caller error; vc_validate_perm
+// detects it) is read as token 0, so no gather leaves the head's rows.
 __device__ __forceinline__ int dq_token(const int32_t* perm, int bh, int N, int pos) {
-  return perm ? perm[(size_t)bh * N + pos] : pos;
+  if (!perm) return pos;
+  const int t = perm[(size_t)bh * N + pos];
+  return (unsigned)t < (unsigned)N ? t : 0;
 }
 
 __device__ __forceinline__ void load4(const uint16_t* p, float* v) {

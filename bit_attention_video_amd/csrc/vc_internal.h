@@ -28,6 +28,8 @@ struct vc_dq_ws {
 vc_dq_ws vc_dq_ws_layout(int BH, int N);
 
 constexpr int VC_SORT_TILE = 1024;   // tokens per sort workgroup
+// VC_OK for hipSuccess, else VC_ERR_HIP with the error kept for vc_last_hip_error().
+int vc_hip_status(hipError_t e);
 constexpr int VC_KSTAT_CHUNK = 1024; // rows per key-mean partial
 
 hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t s);
@@ -62,7 +64,15 @@ hipError_t vc_launch_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const u
                                   int BH, int N, float L4, unsigned flags, uint16_t* O,
                                   hipStream_t s);  // L4 = float32(log2(e) softmax_scale)
 
+// clk: NULL, or 4 x vc_attn_fwd_workgroups(BH, N) uint64 that receive each workgroup's start
+// and end stamps (shader cycles, constant-rate ticks) for the clock probe.
 hipError_t vc_launch_attn_fwd(const uint16_t* Q, const uint8_t* Kq, const float* sK,
                               const uint8_t* Rq, const uint16_t* mu, const float* sV,
                               int BH, int N, float L, unsigned flags, uint16_t* O,
-                              hipStream_t s);  // L = float32(8 log2(e) softmax_scale)
+                              uint64_t* clk, hipStream_t s);  // L = float32(8 log2(e) softmax_scale)
+uint32_t vc_attn_fwd_workgroups(int BH, int N);
+hipError_t vc_launch_test_qquant(const uint16_t* Q, int BH, int N, float L, bool hadamard, uint8_t* Qq, float* sQ,
+                                 hipStream_t s);
+// Per (b,h): count of entries of perm [BH][N] outside [0, N) or repeated, into bad [BH]; bits is
+// a scratch bitmap of BH * ceil(N/32) words.
+hipError_t vc_launch_validate_perm(const int32_t* perm, int BH, int N, uint32_t* bits, int32_t* bad, hipStream_t s);

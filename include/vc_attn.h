@@ -59,6 +59,13 @@ enum vc_status {
                                        "exp-then-cast" comparator, Table 4's naive FP8) */
 #define VC_ATTN_HADAMARD 0x4u    /* rotate Q L by H before quantising (App. B's Q pass, the fused
                                     QK Hadamard of Sec. 4.1); pair with VC_DQ_HADAMARD keys */
+/* vc_workspace_size operations */
+#define VC_OP_GROUP 1             /* vc_vsmooth_group (uses k) */
+#define VC_OP_DEMEAN_QUANT 2      /* vc_vsmooth_demean_quant */
+#define VC_OP_DEMEAN_QUANT_MX4 3  /* vc_vsmooth_demean_quant_mx4 */
+#define VC_OP_ATTN_FWD 4          /* vc_attn_fwd (needs none: 0) */
+#define VC_OP_ATTN_FWD_MX4 5      /* vc_attn_fwd_mx4 (needs none: 0) */
+#define VC_OP_VALIDATE_PERM 6     /* vc_validate_perm */
 /* vc_vsmooth_demean_quant flags */
 #define VC_DQ_NO_DEMEAN 0x1u     /* mu = 0: quantise V' itself (unsmoothed per-channel baseline) */
 #define VC_DQ_HADAMARD 0x2u      /* quantise the rotated keys K' H, scale / 128 (App. B's K pass) */
@@ -68,6 +75,12 @@ const char* vc_strerror(int status);
 
 /* hipError_t of the last VC_ERR_HIP returned on the calling thread (0 if none). */
 int vc_last_hip_error(void);
+
+/* Bytes of scratch the call `op` (VC_OP_*) needs for this shape, 256-byte aligned; one entry for
+ * all calls (the per-call *_workspace_size functions give the same numbers).  0 when the call
+ * needs none, for an empty shape, for d != 128 or for an unknown op.  k is used by VC_OP_GROUP
+ * only (an invalid k sizes for k = 256; the call itself then rejects it). */
+size_t vc_workspace_size(int op, int B, int H, int N, int d, int k);
 
 /* ------------------------------------------------------------------------------------------
  * Grouping: k-means over value tokens and the label sort (Sec. 3.2, "Value-guided
@@ -122,7 +135,10 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
  *
  *   K, V     in   bf16 [B,H,N,d]
  *   perm     in   int32 [B,H,N] permutation of 0..N-1 per (b,h), or NULL for identity.
- *                 Entries are not checked; values outside [0, N) are undefined behaviour.
+ *                 Entries are not validated here (vc_validate_perm does that); an entry outside
+ *                 [0, N) is read as token 0, so every gather stays inside the head's rows, and a
+ *                 repeated entry repeats its token: the outputs are then not those of any
+ *                 permutation, but nothing outside K and V is read.
  *   Kq       out  E4M3 bytes [B,H,N,d]
  *   sK       out  float32 [B,H,N/128]
  *   Rq       out  E4M3 bytes, TILE-TRANSPOSED: [B,H,N/128][d][128 slots].  Within tile j,
@@ -216,6 +232,21 @@ int vc_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4, c
                     float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Validation of a caller's permutation (Sec. 3.2, Eq. 3: pi must reorder the N keys and values
+ * of each (b,h) jointly, without loss or repetition).
+ *
+ *   perm  in   int32 [B,H,N]
+ *   bad   out  int32 [B,H] (device): per (b,h) the number of entries outside [0, N) plus, for
+ *              every value that occurs c > 1 times, c - 1.  0 exactly when perm[b,h] is a
+ *              permutation of 0..N-1.  Deterministic.
+ *   ws    scratch of vc_workspace_size(VC_OP_VALIDATE_PERM, B, H, N, 128, 0) bytes
+ * Errors: VC_ERR_SHAPE for negative sizes, VC_ERR_OVERFLOW for B*H*N >= 2^31, VC_ERR_NULL,
+ * VC_ERR_WORKSPACE.  Every read stays inside perm.
+ * -------------------------------------------------------------------------------------- */
+int vc_validate_perm(const int32_t* perm, int B, int H, int N, int32_t* bad, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Test hooks: single stages of the path, exposed so each can be checked on its own.
  * -------------------------------------------------------------------------------------- */
 
@@ -257,6 +288,29 @@ int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_
  * workgroups < 1, iters < 1 or a FLOP count beyond 2^62, VC_ERR_HIP if the counter rate
  * cannot be read. */
 int vc_test_mfma_fp8_rate(float* out, int workgroups, int iters, float* clock_mhz, hipStream_t stream);
+
+/* The query prologue of vc_attn_fwd run on its own (App. B's Q pass; row a8 of the path): per
+ * 128-row block of X = float32(Q L) (rotated by H with VC_ATTN_HADAMARD), sQ = 2^E the smallest
+ * power of two with amax|X| <= 448 sQ, Qq = E4M3_RNE(X / sQ), with the kernel's own code.
+ *   Qq out E4M3 bytes [B,H,N,d] (natural layout);  sQ out float32 [B,H,N/128].
+ * flags: VC_ATTN_HADAMARD only.  softmax_scale as vc_attn_fwd. */
+int vc_test_quantize_q(const uint16_t* Q, int B, int H, int N, int d, float softmax_scale, unsigned flags,
+                       uint8_t* Qq, float* sQ, hipStream_t stream);
+
+/* Clock probe of the attention kernel: vc_attn_fwd's kernel with its stamps switched on.  The
+ * first wave of workgroup g reads the shader-cycle counter (s_memtime) and the constant-rate
+ * counter (s_memrealtime, hipDeviceAttributeWallClockRate ticks per second) at its start and at
+ * its end and writes them to clk[4 g .. 4 g + 3] = (cycles, ticks) at the start, then at the
+ * end (uint64, device), so sum(cycles) / sum(ticks) x rate over the workgroups is the shader
+ * clock the kernel ran at.  O and every other argument as vc_attn_fwd; clk needs
+ * vc_test_attn_clock_slots(B,H,N) entries. */
+size_t vc_test_attn_clock_slots(int B, int H, int N);
+/* Rate of the constant-rate counter of the current device in kHz (hipDeviceAttributeWallClockRate),
+ * into *khz.  VC_ERR_NULL for a null khz, VC_ERR_HIP if the attribute cannot be read. */
+int vc_test_wall_clock_khz(int* khz);
+int vc_test_attn_fwd_clock(const uint16_t* Q, const uint8_t* Kq, const float* sK, const uint8_t* Rq,
+                           const uint16_t* mu, const float* sV, int B, int H, int N, int d,
+                           float softmax_scale, unsigned flags, uint16_t* O, uint64_t* clk, hipStream_t stream);
 
 #ifdef __cplusplus
 }

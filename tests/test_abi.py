@@ -178,3 +178,48 @@ def test_rq_layout_roundtrip_and_key_order():
     assert vc.KEY_OF_SLOT[0] == 0 and vc.KEY_OF_SLOT[1] == 1 and vc.KEY_OF_SLOT[4] == 8
     assert vc.KEY_OF_SLOT[16] == 32 and vc.KEY_OF_SLOT[32] == 4 and vc.KEY_OF_SLOT[64] == 64
     assert np.array_equal(T[0, 1, 2, 5, :].numpy(), R[0, 1, 256 + vc.KEY_OF_SLOT, 5].numpy())   # [.., c, s]
+
+
+def test_workspace_size_entry_matches_per_call_sizes():
+    lib = vc.lib()
+    for B, H, N, k in [(1, 8, 8192, 64), (1, 40, 70016, 128), (2, 3, 384, 7)]:
+        assert lib.vc_workspace_size(vc.VC_OP_GROUP, B, H, N, 128, k) == lib.vc_group_workspace_size(B, H, N, k)
+        dq = lib.vc_demean_quant_workspace_size(B, H, N)
+        assert lib.vc_workspace_size(vc.VC_OP_DEMEAN_QUANT, B, H, N, 128, 0) == dq
+        assert lib.vc_workspace_size(vc.VC_OP_DEMEAN_QUANT_MX4, B, H, N, 128, 0) == dq
+        assert lib.vc_workspace_size(vc.VC_OP_ATTN_FWD, B, H, N, 128, 0) == 0
+        assert lib.vc_workspace_size(vc.VC_OP_ATTN_FWD_MX4, B, H, N, 128, 0) == 0
+        v = lib.vc_workspace_size(vc.VC_OP_VALIDATE_PERM, B, H, N, 128, 0)
+        assert v >= B * H * ((N + 31) // 32) * 4 and v % 256 == 0
+    assert lib.vc_workspace_size(vc.VC_OP_GROUP, 1, 1, 1024, 64, 8) == 0      # d != 128
+    assert lib.vc_workspace_size(99, 1, 1, 1024, 128, 8) == 0                 # unknown op
+    assert lib.vc_workspace_size(vc.VC_OP_VALIDATE_PERM, 1, 0, 1024, 128, 0) == 0
+
+
+def test_validate_perm_argument_errors():
+    lib = vc.lib()
+    f = lib.vc_validate_perm
+    ws = lib.vc_workspace_size(vc.VC_OP_VALIDATE_PERM, 1, 2, 1000, 128, 0)
+    assert f(FAKE, -1, 2, 1000, FAKE, FAKE, ws, None) == S["VC_ERR_SHAPE"]
+    assert f(FAKE, 1, 1 << 16, 1 << 16, FAKE, FAKE, ws, None) == S["VC_ERR_OVERFLOW"]
+    assert f(None, 1, 2, 1000, FAKE, FAKE, ws, None) == S["VC_ERR_NULL"]
+    assert f(FAKE, 1, 2, 1000, None, FAKE, ws, None) == S["VC_ERR_NULL"]
+    assert f(FAKE, 1, 2, 1000, FAKE, FAKE, ws - 1, None) == S["VC_ERR_WORKSPACE"]
+    assert f(None, 1, 2, 0, None, None, 0, None) == S["VC_OK"]      # any N works, empty is a no-op
+
+
+def test_new_hook_argument_errors():
+    lib = vc.lib()
+    q = lib.vc_test_quantize_q
+    assert q(FAKE, 1, 1, 100, 128, 0.0, 0, FAKE, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert q(None, 1, 1, 128, 128, 0.0, 0, FAKE, FAKE, None) == S["VC_ERR_NULL"]
+    assert q(FAKE, 1, 1, 128, 128, 0.0, vc.VC_ATTN_NO_MEAN, FAKE, FAKE, None) == S["VC_ERR_FLAGS"]
+    assert q(FAKE, 1, 1, 128, 128, -2.0, vc.VC_ATTN_HADAMARD, FAKE, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert q(None, 1, 1, 0, 128, 0.0, 0, None, None, None) == S["VC_OK"]
+    c = lib.vc_test_attn_fwd_clock
+    P = [FAKE] * 6
+    assert lib.vc_test_attn_clock_slots(1, 40, 70016) == 4 * 40 * 274
+    assert lib.vc_test_attn_clock_slots(1, 1, 100) == 0
+    assert c(*P, 1, 1, 128, 128, 0.0, 0, FAKE, None, None) == S["VC_ERR_NULL"]      # clk required
+    assert c(*P, 1, 1, 128, 64, 0.0, 0, FAKE, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert c(*P, 1, 1, 128, 128, 0.0, 0x10, FAKE, FAKE, None) == S["VC_ERR_FLAGS"]

@@ -192,3 +192,31 @@ def test_demean_quant_bit_exact(name, heads, perm_kind, no_demean):
         assert np.array_equal(sV[0, h], vq["sV"])
         assert np.array_equal(Rq[0, h], vq["codes"])
         assert np.array_equal(mu_bits[0, h], F.bf16_bits_from_value(vq["mu_t"]))
+
+
+def test_zero_residual_channel_and_constant_block():
+    """A channel constant inside every block has no residual: s_V = 1, zero codes, stored mean =
+    bf16(mu) (the V scale's reading for a zero amax); a block constant in every channel gives zero
+    codes.  GPU operands bit-exact against the oracle, attention within the parity tolerance."""
+    from oracle import attention as T
+    rng = np.random.default_rng(42)
+    N = 512
+    Vv = F.bf16_round(rng.standard_normal((N, 128)))
+    Vv[:, 9] = np.repeat(F.bf16_round(rng.standard_normal(N // 128) * 3), 128)
+    Vv[256:384] = F.bf16_round(rng.standard_normal(128))[None, :]
+    Qv = F.bf16_round(rng.standard_normal((N, 128)))
+    Kv = F.bf16_round(rng.standard_normal((N, 128)))
+    bits = lambda x: F.bf16_bits_from_value(x)[None, None]
+    perm = np.arange(N, dtype=np.int32)
+    ops = vc.vc_vsmooth_demean_quant(bf16_dev(bits(Kv)), bf16_dev(bits(Vv)), torch.from_numpy(perm[None, None]).to(DEV))
+    vq = S.quantize_v(Vv, perm)
+    sV = ops["sV"].cpu().numpy()[0, 0]
+    assert sV[9] == 1.0 and np.array_equal(sV, vq["sV"])
+    R = vc.rq_tiled_to_natural(ops["Rq"]).cpu().numpy()[0, 0]
+    assert np.array_equal(R, vq["codes"]) and np.all(R[:, 9] == 0) and np.all((R[256:384] & 0x7F) == 0)
+    mu = values(bf16_host_bits(ops["mu"]))[0, 0]
+    assert np.array_equal(mu, vq["mu_t"])
+    O = values(bf16_host_bits(vc.vc_attn_fwd(bf16_dev(bits(Qv)), ops["Kq"], ops["sK"], ops["Rq"], ops["mu"],
+                                             ops["sV"])))[0, 0]
+    O_ref, _ = T.vc_attention_emulated(Qv, Kv, Vv, perm)
+    assert T.rel_l2(O, O_ref) < 5e-3
