@@ -29,7 +29,8 @@ __all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_
            "VC_ATTN_NO_MEAN", "VC_ATTN_EXP_THEN_CAST", "VC_ATTN_HADAMARD", "VC_DQ_NO_DEMEAN",
            "VC_DQ_HADAMARD", "STATUS", "vc_workspace_size", "vc_validate_perm", "vc_test_quantize_q",
            "vc_test_attn_fwd_clock", "VC_OP_GROUP", "VC_OP_DEMEAN_QUANT", "VC_OP_DEMEAN_QUANT_MX4",
-           "VC_OP_ATTN_FWD", "VC_OP_ATTN_FWD_MX4", "VC_OP_VALIDATE_PERM", "wall_clock_mhz"]
+           "VC_OP_ATTN_FWD", "VC_OP_ATTN_FWD_MX4", "VC_OP_VALIDATE_PERM", "wall_clock_mhz",
+           "vc_vsmooth_group_static"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvcattn.so")
 
@@ -70,6 +71,7 @@ _SIGNATURES = {
     "vc_test_kmeans_assign": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "vc_test_label_sort": (_I, [_P, _I, _I, _I, _I, _P, _P, _P, _Z, _P]),
     "vc_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "vc_vsmooth_group_static": (_I, [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
     "vc_validate_perm": (_I, [_P, _I, _I, _I, _P, _P, _Z, _P]),
     "vc_test_quantize_q": (_I, [_P, _I, _I, _I, _I, _F, _U, _P, _P, _P]),
     "vc_test_attn_clock_slots": (_Z, [_I, _I, _I]),
@@ -154,6 +156,24 @@ def vc_vsmooth_group(V: torch.Tensor, k: int, iters: int, C_init: Optional[torch
     _check(lib().vc_vsmooth_group(_ptr(V), B, H, N, d, k, iters, _ptr(C_init), _ptr(C), _ptr(labels),
                                   _ptr(perm), _ptr(offsets), _ptr(J), _ptr(ws), nws, _stream()),
            "vc_vsmooth_group")
+    return {"C": C, "labels": labels, "perm": perm, "offsets": offsets, "J": J}
+
+
+def vc_vsmooth_group_static(V: torch.Tensor, k: int, iters: int, C_init: Optional[torch.Tensor] = None,
+                            objective: bool = True):
+    """vc_vsmooth_group on the library's own device scratch: the library allocates nothing (the
+    outputs are the caller's).  Calls overlapping on one GPU race on that scratch."""
+    B, H, N, d = _bhnd(V, "V")
+    dev = V.device
+    if C_init is not None:
+        _need(C_init, "C_init", torch.float32, (B, H, k, d))
+    C = torch.empty((B, H, k, d), dtype=torch.float32, device=dev)
+    labels = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    perm = torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    offsets = torch.empty((B, H, k + 1), dtype=torch.int32, device=dev)
+    J = torch.empty((B, H), dtype=torch.float64, device=dev) if objective else None
+    _check(lib().vc_vsmooth_group_static(_ptr(V), B, H, N, d, k, iters, _ptr(C_init), _ptr(C), _ptr(labels),
+                                         _ptr(perm), _ptr(offsets), _ptr(J), _stream()), "vc_vsmooth_group_static")
     return {"C": C, "labels": labels, "perm": perm, "offsets": offsets, "J": J}
 
 

@@ -112,6 +112,21 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
                      int32_t* offsets, double* objective, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* vc_vsmooth_group without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and errors as vc_vsmooth_group minus ws / ws_bytes; the scratch is a
+ * library-held device array of VC_GROUP_STATIC_SCRATCH_BYTES (16 MiB) per GPU, kept until the
+ * process ends.  A shape whose grouping workspace (vc_group_workspace_size) exceeds it returns
+ * VC_ERR_WORKSPACE before any HIP call (e.g. B*H = 40, N = 70,016, k = 128 needs 5.5 MB;
+ * B*H = 24, N = 115,200, k = 256 needs 6.0 MB).  No call allocates or frees.  The first call on a
+ * device resolves the array's address (hipGetSymbolAddress; make it outside graph capture).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (different streams
+ * or threads without ordering) race and must be serialised by the caller. */
+#define VC_GROUP_STATIC_SCRATCH_BYTES (16u << 20)
+int vc_vsmooth_group_static(const uint16_t* V, int B, int H, int N, int d, int k, int iters,
+                            const float* C_init, float* C_out, int32_t* labels, int32_t* perm,
+                            int32_t* offsets, double* objective, hipStream_t stream);
+
 /* ------------------------------------------------------------------------------------------
  * Smoothing and quantisation of K and V in permuted order (Sec. 3.2 Eq. 3-4; App. B).
  *
