@@ -151,6 +151,64 @@ def accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads, nrows=256):
             "kmeans_J_rel_err_max": float(f"{max(r['J']):.3e}")}
 
 
+def time_ms(torch, fn, reps):
+    """Mean launch time of fn() over reps back-to-back calls, HIP events on the current stream."""
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def config_summary(name, vc, torch):
+    """One other workload at its full size, outside the timed region: grouping, demean/quantise and
+    attention each timed over a few launches, and V-Smooth's cost relative to attention.  For the
+    permutation-reuse workload, also the 4-step schedule with a cold and with a warm-started
+    regroup (3 rounds from the previous grouping's centroids, the steady state of a schedule that
+    regroups every 4 steps)."""
+    import synth
+    cfg = synth.get_config(name)
+    B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    to = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    if cfg.steps > 1:
+        Q, K, Vs = synth.make_reuse_steps(cfg)
+        V = Vs[0]
+    else:
+        Q, K, V = synth.make_qkv(cfg)
+    Qd, Kd, Vd = to(Q), to(K), to(V)
+    g = vc.vc_vsmooth_group(Vd, cfg.k, cfg.iters)
+    ops = vc.vc_vsmooth_demean_quant(Kd, Vd, g["perm"])
+    O = vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"])
+    t_group = time_ms(torch, lambda: vc.vc_vsmooth_group(Vd, cfg.k, cfg.iters), 3)
+    t_dq = time_ms(torch, lambda: vc.vc_vsmooth_demean_quant(Kd, Vd, g["perm"]), 5)
+    reps = max(3, int(300.0 / max(1e-3, attn_flops(B, H, N, d) / 2.5e12)))   # ~0.3 s of attention
+    t_attn = time_ms(torch, lambda: vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"],
+                                                   out=O), min(reps, 200))
+    tf = attn_flops(B, H, N, d) / (t_attn * 1e-3) / 1e12
+    out = {"workload": f"{name}: B={B} H={H} N={N} d={d} k={cfg.k}", "attn_ms": round(t_attn, 4),
+           "attn_tflops": round(tf, 2), "frac": round(tf / FP8_PEAK_TFLOPS, 4), "group_ms": round(t_group, 4),
+           "demean_quant_ms": round(t_dq, 4),
+           "vsmooth_over_attn": {"grouping_step": round((t_group + t_dq) / t_attn, 4),
+                                 "schedule_40_steps": round((3 * t_group + 10 * t_dq) / (40 * t_attn), 4)}}
+    if cfg.steps > 1:
+        Vds = [to(v) for v in Vs]
+        t_warm = time_ms(torch, lambda: vc.vc_vsmooth_group(Vds[1], cfg.k, 3, C_init=g["C"]), 3)
+        J_warm = vc.vc_vsmooth_group(Vds[1], cfg.k, 3, C_init=g["C"])["J"].double().mean().item()
+        J_cold = vc.vc_vsmooth_group(Vds[1], cfg.k, cfg.iters)["J"].double().mean().item()
+        S = cfg.steps
+        out["reuse"] = {"steps": S, "warm_regroup_3_rounds_ms": round(t_warm, 4),
+                        "window_cold_regroup": round((t_group + S * t_dq) / (S * t_attn), 4),
+                        "window_warm_regroup": round((t_warm + S * t_dq) / (S * t_attn), 4),
+                        "J_warm_3_over_J_cold_10": round(J_warm / J_cold, 6)}
+        del Vds
+    del Qd, Kd, Vd, ops, O, g
+    torch.cuda.empty_cache()
+    return out
+
+
 def reuse_schedule(args, cfg, vc, torch):
     """The permutation-reuse workload: V drifts over cfg.steps steps; grouping runs on the
     first step only and pi is reused (the pages' amortisation, Sec. 3.4).  Also times a
@@ -227,6 +285,7 @@ def reuse_schedule(args, cfg, vc, torch):
             "warm_regroup_3_rounds_ms": round(t_warm, 4),
             "warm_over_cold_group_time": round(t_warm / t_group, 4),
             "J_warm_3_over_J_cold_10": round(J_warm / J_cold, 6),
+            "vsmooth_over_attn_reuse_window_warm": round((t_warm + cfg.steps * t_dq) / (cfg.steps * t_attn), 4),
         },
     }
     if not args.no_cpu_baseline:
@@ -243,6 +302,7 @@ def main():
     ap.add_argument("--config", default="video")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true", help="skip the oracle accuracy report")
+    ap.add_argument("--no-configs", action="store_true", help="skip the medium, reuse and long summaries")
     ap.add_argument("--attn-only-iters", type=int, default=0,
                     help="extra back-to-back vc_attn_fwd launches timed alone (for profiling)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -443,6 +503,12 @@ def main():
                         "attn_over_unrotated": round(t_attn_rot / t_attn, 4),
                         "demean_quant_over_unrotated": round(t_dq_rot / t_dq, 4)},
     }
+    if not args.no_configs:
+        out["configs"] = {}
+        for name in ("medium", "reuse", "long"):
+            log(f"workload {name} (outside the timed region)")
+            out["configs"][name] = config_summary(name, vc, torch)
+            log(f"{name}: {json.dumps(out['configs'][name])}")
     if not args.no_accuracy:
         log("accuracy on sampled heads (oracle, outside the timed region)")
         base = vc.vc_vsmooth_demean_quant(Kd, Vd, None, no_demean=True)

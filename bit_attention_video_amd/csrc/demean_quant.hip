@@ -11,8 +11,9 @@
 //   k_kstat_partial  float64 channel sums of K per 1024-row chunk
 //   k_kstat_final    kbar = float32(sum / N) in chunk order
 //   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = 2^E (smallest power of two
-//                    with amax <= 448 sK, an E8M0 block scale), codes; with VC_DQ_HADAMARD the
-//                    rows K' H (Sylvester H, App. B) are quantised and sK = 2^(E-7)
+//                    with amax <= 448 sK, an E8M0 block scale), codes
+//   k_kquant_had     the same with VC_DQ_HADAMARD: the rows K' H (Sylvester H, App. B) are
+//                    quantised and sK = 2^(E-7)
 //   k_vpass1         per block of V[pi]: mu_j (float64 sum / 128), the block's |R| maxima
 //   k_vamax          per-channel maximum over each eighth of the blocks (no atomics)
 //   k_vpass2         sV = (maximum of the eight) / 448; codes of R / sV into the tile-transposed
@@ -120,10 +121,8 @@ __device__ __forceinline__ void hadamard_k_row(float* x, int q4) {
   x[3] = (float)a3;
 }
 
-// HAD: codes of (K[pi] - kbar) H; the stored scale is 2^(E-7), carrying the 1/128 of H / 128.
 // 512 threads per 128-row block: thread (q4, rg) takes channels 4 q4 .. 4 q4 + 3 of rows
 // rg + 16 i, i < 8 (few registers per thread, so many blocks stream at once).
-template <bool HAD>
 __global__ __launch_bounds__(512) void k_kquant(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
                                                 const float* __restrict__ kbar, int N,
                                                 uint8_t* __restrict__ Kq, float* __restrict__ sK) {
@@ -142,34 +141,98 @@ __global__ __launch_bounds__(512) void k_kquant(const uint16_t* __restrict__ K, 
     x[i][1] = v[1] - kb.y;
     x[i][2] = v[2] - kb.z;
     x[i][3] = v[3] - kb.w;
-    if constexpr (!HAD)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
-  }
-  if constexpr (HAD) {
-    // two rows at a time: interleaving all rows' exchanges would need eight live float64 sets
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      hadamard_k_row(x[i], q4);
-      hadamard_k_row(x[i + 1], q4);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
+    for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(x[i][e]));
   }
   amax = block_max_512(amax, red8);
   const int E = pow2_block_exponent(amax);
   const float inv = __builtin_ldexpf(1.0f, -E);   // exact: the scale is a power of two
-  const float s = __builtin_ldexpf(1.0f, HAD ? E - 7 : E);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int r = j * VC_BLK + rg + 16 * i;
     const uint32_t w = e4m3x4(x[i][0] * inv, x[i][1] * inv, x[i][2] * inv, x[i][3] * inv);
     *(uint32_t*)(Kq + ((size_t)bh * N + r) * VC_D + 4 * q4) = w;
   }
-  if (t == 0) sK[(size_t)bh * (N / VC_BLK) + j] = s;
+  if (t == 0) sK[(size_t)bh * (N / VC_BLK) + j] = __builtin_ldexpf(1.0f, E);
+}
+
+// The rotated K pass (VC_DQ_HADAMARD): 4 lanes per row, lane (row, c4) holding channels
+// 32 c4 .. 32 c4 + 31 as y[i] (channel bits 0-4 local, bits 5-6 the lane's bits 0-1).  Five
+// butterfly stages run in registers and two across the lanes of a quad (DPP quad permutes, no
+// LDS traffic).  float64 throughout: the signed sum of the 128 float32 terms is exact whatever
+// the order, so each rotated value is float32(exact K' H) and the codes match the oracle bit for
+// bit.  The stored scale is 2^(E-7), carrying the 1/128 of H / 128.
+__device__ __forceinline__ double dpp_quad_xor(double v, int m) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const int lo = (int)(uint32_t)u, hi = (int)(uint32_t)(u >> 32);
+  int rlo, rhi;
+  if (m == 1) {   // quad_perm [1,0,3,2]
+    rlo = __builtin_amdgcn_mov_dpp(lo, 0xB1, 0xF, 0xF, false);
+    rhi = __builtin_amdgcn_mov_dpp(hi, 0xB1, 0xF, 0xF, false);
+  } else {        // quad_perm [2,3,0,1]
+    rlo = __builtin_amdgcn_mov_dpp(lo, 0x4E, 0xF, 0xF, false);
+    rhi = __builtin_amdgcn_mov_dpp(hi, 0x4E, 0xF, 0xF, false);
+  }
+  return __builtin_bit_cast(double, ((uint64_t)(uint32_t)rhi << 32) | (uint32_t)rlo);
+}
+
+__global__ __launch_bounds__(512) void k_kquant_had(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
+                                                    const float* __restrict__ kbar, int N,
+                                                    uint8_t* __restrict__ Kq, float* __restrict__ sK) {
+  __shared__ float red8[8];
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int row = t >> 2, c4 = t & 3;
+  const int tok = dq_token(perm, bh, N, j * VC_BLK + row);
+  const uint4* src = (const uint4*)(K + ((size_t)bh * N + tok) * VC_D + 32 * c4);
+  const float* kb = kbar + (size_t)bh * VC_D + 32 * c4;
+  double y[32];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint4 raw = src[v];
+    const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    const float4 k0 = *(const float4*)(kb + 8 * v), k1 = *(const float4*)(kb + 8 * v + 4);
+    const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[8 * v + 2 * e] = (double)(bf16_to_f32(wd[e] & 0xFFFFu) - kk[2 * e]);       // float32 K' = K - kbar
+      y[8 * v + 2 * e + 1] = (double)(bf16_to_f32(wd[e] >> 16) - kk[2 * e + 1]);
+    }
+  }
+#pragma unroll
+  for (int b = 1; b < 32; b <<= 1)
+#pragma unroll
+    for (int k = 0; k < 32; ++k)
+      if (!(k & b)) {
+        const double u = y[k], v = y[k | b];
+        y[k] = u + v;
+        y[k | b] = u - v;
+      }
+#pragma unroll
+  for (int m = 1; m <= 2; m <<= 1) {
+    const bool upper = c4 & m;   // this lane holds the partner with channel bit set
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const double o = dpp_quad_xor(y[k], m);
+      y[k] = upper ? o - y[k] : y[k] + o;
+    }
+  }
+  float z[32];
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    z[k] = (float)y[k];
+    amax = fmaxf(amax, fabsf(z[k]));
+  }
+  amax = block_max_512(amax, red8);
+  const int E = pow2_block_exponent(amax);
+  const float inv = __builtin_ldexpf(1.0f, -E);   // exact: the scale is a power of two
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = e4m3x4(z[4 * i] * inv, z[4 * i + 1] * inv, z[4 * i + 2] * inv, z[4 * i + 3] * inv);
+  uint4* dst = (uint4*)(Kq + ((size_t)bh * N + j * VC_BLK + row) * VC_D + 32 * c4);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  if (t == 0) sK[(size_t)bh * (N / VC_BLK) + j] = __builtin_ldexpf(1.0f, E - 7);
 }
 
 // amax[bh][g][c] = max over tiles j in slice g (of 8) of amaxp[bh][j][c]; 128 threads per
@@ -349,7 +412,7 @@ __global__ __launch_bounds__(256) void k_kquant4(const uint16_t* __restrict__ K,
   const size_t row0 = (size_t)bh * N + j * VC_BLK + rg;
 #pragma unroll
   for (int i = 0; i < 16; i += 2) {
-    if constexpr (HAD) {   // two rows per scheduling region, as in k_kquant
+    if constexpr (HAD) {   // two rows per scheduling region (32 lanes per row)
       hadamard_k_row(x[i], q4);
       hadamard_k_row(x[i + 1], q4);
     }
@@ -468,9 +531,9 @@ hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const in
   hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
   if (flags & VC_DQ_HADAMARD)
-    hipLaunchKernelGGL(k_kquant<true>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
+    hipLaunchKernelGGL(k_kquant_had, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
   else
-    hipLaunchKernelGGL(k_kquant<false>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
+    hipLaunchKernelGGL(k_kquant, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);
   float* amax = (float*)(ws + L.amax);
   hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(512), 0, s, V, perm, N,
                      (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amaxp);
