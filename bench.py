@@ -209,6 +209,81 @@ def config_summary(name, vc, torch):
     return out
 
 
+def diagnostics():
+    """The pages' error diagnostics on sampled heads of the medium, video and long workloads, of the
+    Q/K channel-outlier workload (where a QK rotation has something to remove) and the reuse
+    workload's warm start, computed by the oracle alone on the CPU: Eq. 2's split of the
+    output error, the block-mean energy share and the value error by token order (Eq. 5, Fig. 4,
+    Table 1), and the row total variation of ExpCast (Sec. 3.3).  One JSON line."""
+    import synth
+    from oracle import diagnostics as D
+    from oracle import vsmooth as S
+    plan = {"medium": [0, 4], "video": [0, 20], "long": [0, 12], "qk_outlier": [0, 2]}
+    res = {}
+    for name, heads in plan.items():
+        cfg = synth.get_config(name)
+        log(f"diagnostics: {name} heads {heads}")
+        Qb, Kb, Vb = synth.make_qkv(cfg, heads)
+        acc = {}
+        for i, h in enumerate(heads):
+            Q, K, V = (synth.bits_to_f32(x[0, i]).astype(np.float64) for x in (Qb, Kb, Vb))
+            perm = S.vsmooth_group(V, cfg.k, cfg.iters)["perm"]
+            cube = D.static_cube_order(cfg.grid, cfg.N)
+            seq = np.arange(cfg.N)
+            rows = np.sort(np.random.default_rng([cfg.cfg_id, h, 9]).choice(cfg.N, 256, replace=False))
+            r = {"mean_share_sequence": D.block_mean_share(V[seq]),
+                 "mean_share_static_cube": D.block_mean_share(V[cube]),
+                 "mean_share_kmeans": D.block_mean_share(V[perm]),
+                 "value_rmse_sequence": D.value_rel_mse(V, seq),
+                 "value_rmse_hadamard_on_v": D.value_rel_mse(V, seq, rotate=True),
+                 "value_rmse_static_cube": D.value_rel_mse(V, cube),
+                 "value_rmse_kmeans": D.value_rel_mse(V, perm)}
+            for tag, p_, dm in (("unsmoothed", None, False), ("vc", perm, True)):
+                for rot in (False, True):
+                    t = D.output_error_terms(Q, K, V, p_, rows, demean=dm, hadamard_qk=rot)
+                    key = f"eq2_{tag}{'_qk_rotated' if rot else ''}"
+                    for k2 in ("prob_term", "value_term", "value_share"):
+                        r[f"{key}_{k2}"] = t[k2]
+            tvr = D.row_tv(Q, K, rows)
+            clean = tvr["tau"] < 1e-9
+            r.update({"tv_expcast_mean": float(tvr["tv_expcast"].mean()), "tv_expcast_max": float(tvr["tv_expcast"].max()),
+                      "tv_expcast_mean_no_underflow": float(tvr["tv_expcast"][clean].mean()) if clean.any() else None,
+                      "tv_expcast_max_no_underflow": float(tvr["tv_expcast"][clean].max()) if clean.any() else None,
+                      "tv_exp_then_cast_mean": float(tvr["tv_exp_then_cast"].mean()),
+                      "rows_with_underflow": int((~clean).sum()),
+                      "rows_over_0.0364_plus_tau": int((tvr["tv_expcast"] >= 0.0364 + tvr["tau"]).sum())})
+            for k2, v in r.items():
+                acc.setdefault(k2, []).append(v)
+            log(f"  head {h}: " + json.dumps({k2: (round(v, 6) if isinstance(v, float) else v) for k2, v in r.items()}))
+        agg = {}
+        for k2, v in acc.items():
+            v = [x for x in v if x is not None]
+            if not v:
+                agg[k2] = None
+            elif k2.endswith("_max") or k2.endswith("_max_no_underflow"):
+                agg[k2] = round(float(max(v)), 6)
+            elif k2.startswith("rows_"):
+                agg[k2] = int(sum(v))
+            else:
+                agg[k2] = round(float(np.mean(v)), 6)
+        res[name] = {"workload": f"{name}: H={cfg.H} N={cfg.N} k={cfg.k}", "heads": heads, "rows_per_head": 256, **agg}
+    # warm start (Table 1's warm-started row): step 1 of the reuse workload grouped by 3 rounds from
+    # step 0's centroids, against a cold 10-round grouping of step 1
+    cfg = synth.get_config("reuse")
+    log("diagnostics: reuse head 0, warm start")
+    Qb, Kb, Vs = synth.make_reuse_steps(cfg, [0])
+    V0, V1 = (synth.bits_to_f32(v[0, 0]).astype(np.float64) for v in Vs[:2])
+    g0 = S.vsmooth_group(V0, cfg.k, cfg.iters)
+    warm = S.vsmooth_group(V1, cfg.k, 3, C_init=g0["C"])
+    cold = S.vsmooth_group(V1, cfg.k, cfg.iters)
+    res["reuse"] = {"workload": f"reuse: H={cfg.H} N={cfg.N} k={cfg.k}, step 1 of head 0",
+                    "value_rmse_sequence": round(D.value_rel_mse(V1, None), 6),
+                    "value_rmse_kmeans": round(D.value_rel_mse(V1, cold["perm"]), 6),
+                    "value_rmse_kmeans_warm_3_rounds": round(D.value_rel_mse(V1, warm["perm"]), 6),
+                    "value_rmse_previous_step_pi": round(D.value_rel_mse(V1, g0["perm"]), 6)}
+    print(json.dumps({"diagnostics": res, "data": "synthetic", "kind": "oracle (CPU)"}), flush=True)
+
+
 def reuse_schedule(args, cfg, vc, torch):
     """The permutation-reuse workload: V drifts over cfg.steps steps; grouping runs on the
     first step only and pi is reused (the pages' amortisation, Sec. 3.4).  Also times a
@@ -303,11 +378,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-accuracy", action="store_true", help="skip the oracle accuracy report")
     ap.add_argument("--no-configs", action="store_true", help="skip the medium, reuse and long summaries")
+    ap.add_argument("--diagnostics", action="store_true",
+                    help="only the oracle's error diagnostics on sampled heads (CPU, no GPU)")
     ap.add_argument("--attn-only-iters", type=int, default=0,
                     help="extra back-to-back vc_attn_fwd launches timed alone (for profiling)")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
+    if args.diagnostics:
+        return diagnostics()
     if args.copy_calib_mib:
         import torch
         n = args.copy_calib_mib << 20

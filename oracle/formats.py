@@ -95,6 +95,40 @@ def e2m1_encode(x) -> np.ndarray:
     return np.where(neg, code | 0x8, code).astype(np.uint8)
 
 
+E2M3_MAX = 7.5
+
+
+def e2m3_decode(codes) -> np.ndarray:
+    """E2M3 (OCP MX FP6) codes (low six bits of uint8) -> float64 values, from the field layout:
+    sign bit 5, exponent field e = bits 4-3 (bias 1), mantissa m = bits 2-0; 2^(e-1) (1 + m/8)
+    for e >= 1, m/8 for e = 0.  No infinities or NaNs; the largest magnitude is 7.5."""
+    c = np.asarray(codes, dtype=np.int64) & 0x3F
+    sign = np.where(c & 0x20, -1.0, 1.0)
+    e = (c >> 3) & 0x3
+    m = (c & 0x7).astype(np.float64)
+    val = np.where(e == 0, m / 8.0, np.ldexp(1.0 + m / 8.0, (e - 1).astype(np.int64)))
+    return sign * val
+
+
+_E2M3_POS = e2m3_decode(np.arange(32))      # 0, 0.125, ..., 0.875, 1, 1.125, ..., 7.5
+
+
+def e2m3_encode(x) -> np.ndarray:
+    """Values -> E2M3 codes (uint8, 0..63): nearest value, ties to the even code, saturating at
+    +-7.5; the sign bit is the input's (a negative value that rounds to zero gives 0x20)."""
+    x = np.asarray(x, dtype=np.float64)
+    neg = np.signbit(x)
+    a = np.minimum(np.abs(x), E2M3_MAX)
+    hi = np.minimum(np.searchsorted(_E2M3_POS, a, side="left"), 31)
+    lo = np.maximum(hi - 1, 0)
+    dlo = a - _E2M3_POS[lo]
+    dhi = _E2M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == _E2M3_POS[hi], hi, code).astype(np.uint8)
+    return np.where(neg, code | 0x20, code).astype(np.uint8)
+
+
 def fl32(x) -> np.ndarray:
     """Round to the nearest float32 (ties to even); returned as float32."""
     return np.asarray(x, dtype=np.float64).astype(np.float32)

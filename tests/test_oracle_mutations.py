@@ -140,24 +140,38 @@ MUTANTS = [
     ("key_group_bit3", "oracle.mx4", "key_group", "return 2 * (k // 64) + ((k >> 2) & 1)",
      "return 2 * (k // 64) + ((k >> 3) & 1)",
      [("test_oracle_mx4", "test_key_groups_are_the_pv_operand_slot_groups", {})]),
-    ("p4_row_max", "oracle.mx4", "quantize_p4", "mx_exponent(P[:, cols].max(axis=1))", "mx_exponent(P.max(axis=1))",
+    ("p4_row_max", "oracle.mx4", "quantize_p4", "mx_exponent(P[:, cols].max(axis=1), fmt)", "mx_exponent(P.max(axis=1), fmt)",
      [("test_oracle_mx4", "test_quantize_p4_brute_force", {})]),
     ("mx4_alpha_sign", "oracle.mx4", "attention_tiled_mx4", "alpha = np.exp2(m - m_new)", "alpha = np.exp2(m_new - m)",
      [("test_oracle_mx4", "test_tiled_exact_mode_is_exact_attention", {})]),
     ("mx4_p_unquantised", "oracle.mx4", "attention_tiled_mx4",
-     "P = quantize_p4(fl32(np.exp2(fl32(s - m_new[:, None]).astype(np.float64))))",
+     "P = quantize_p4(fl32(np.exp2(fl32(s - m_new[:, None]).astype(np.float64))), fmt)",
      "P = fl32(np.exp2(fl32(s - m_new[:, None]).astype(np.float64))).astype(np.float64)",
      [("test_oracle_mx4", "test_mx4_recurrence_closed_form", {})]),
     ("mx4_mean_term_dropped", "oracle.mx4", "attention_tiled_mx4", " + r[:, None] * mu_b[j][None, :]", "",
      [("test_oracle_mx4", "test_tiled_exact_mode_is_exact_attention", {})]),
-    ("v4_signed_max", "oracle.mx4", "quantize_v4", "mx_exponent(np.abs(R[:, rows, :]).max(axis=1))",
-     "mx_exponent(R[:, rows, :].max(axis=1))", [("test_oracle_mx4", "test_v4_quantiser_groups_and_bound", {})]),
+    ("v4_signed_max", "oracle.mx4", "quantize_v4", "mx_exponent(np.abs(R[:, rows, :]).max(axis=1), fmt)",
+     "mx_exponent(R[:, rows, :].max(axis=1), fmt)", [("test_oracle_mx4", "test_v4_quantiser_groups_and_bound", {})]),
     ("q4_without_slope", "oracle.mx4", "quantize_q4", "X = (fl32(Q) * log2e_scale4(softmax_scale, Q.shape[1])).astype(np.float32)",
      "X = fl32(Q).astype(np.float32)", [("test_oracle_mx4", "test_q4_k4_quantisers_fold_slope_and_centre", {})]),
     ("k4_not_centred", "oracle.mx4", "quantize_k4", "Ks = (Kp - kbar[None, :]).astype(np.float32)",
      "Ks = Kp.astype(np.float32)", [("test_oracle_mx4", "test_q4_k4_quantisers_fold_slope_and_centre", {})]),
     ("k4_rotation_exponent", "oracle.mx4", "quantize_k4", "return codes, E - 7", "return codes, E",
      [("test_oracle_mx4", "test_k4_rotated_keys_are_the_centred_keys_times_h_over_d", {})]),
+    # diagnostics
+    ("cube_inner_first", "oracle.diagnostics", "static_cube_order", "np.lexsort((inner, cid))",
+     "np.lexsort((cid, inner))", [("test_oracle_diagnostics", "test_static_cube_order_is_a_permutation_of_whole_cubes", {})]),
+    ("share_of_residual", "oracle.diagnostics", "block_mean_share", "block_energy_split(Vp[j * BV:(j + 1) * BV])[4]",
+     "block_energy_split(Vp[j * BV:(j + 1) * BV])[3]", [("test_oracle_diagnostics", "test_block_mean_share_extremes", {})]),
+    ("dequant_without_mean", "oracle.diagnostics", "dequantized_v", "(codes + mu_rows)", "codes",
+     [("test_oracle_diagnostics", "test_value_error_of_grid_values_is_zero_and_bounded_otherwise", {})]),
+    ("value_error_unpermuted", "oracle.diagnostics", "value_rel_mse", "Vp = fl32(V[perm])", "Vp = fl32(V)",
+     [("test_oracle_diagnostics", "test_value_error_falls_with_value_grouping", {}),
+      ("test_oracle_diagnostics", "test_value_error_of_grid_values_is_zero_and_bounded_otherwise", {})]),
+    ("eq2_value_term_sign", "oracle.diagnostics", "output_error_terms", "np.linalg.norm(PqV - Oq)",
+     "np.linalg.norm(PqV + Oq)", [("test_oracle_diagnostics", "test_eq2_terms_add_up_and_value_term_vanishes_on_grid_values", {})]),
+    ("tv_natural_exp", "oracle.diagnostics", "row_tv", "p = np.exp2(u)", "p = np.exp(u)",
+     [("test_oracle_diagnostics", "test_row_tv_obeys_prop31_and_the_e4m3_bound", {})]),
 ]
 
 _PIN_OK = {}
@@ -230,4 +244,4 @@ def test_planted_mistake_fails_a_pin(mid, mod_name, fn_name, old, new, pins):
 def test_every_oracle_module_is_mutated():
     mods = {m[1] for m in MUTANTS}
     assert mods == {"oracle.formats", "oracle.expcast", "oracle.analysis", "oracle.attention",
-                    "oracle.vsmooth", "oracle.rotation", "oracle.mx4"}
+                    "oracle.vsmooth", "oracle.rotation", "oracle.mx4", "oracle.diagnostics"}
