@@ -158,6 +158,10 @@ MUTANTS = [
      "Ks = Kp.astype(np.float32)", [("test_oracle_mx4", "test_q4_k4_quantisers_fold_slope_and_centre", {})]),
     ("k4_rotation_exponent", "oracle.mx4", "quantize_k4", "return codes, E - 7", "return codes, E",
      [("test_oracle_mx4", "test_k4_rotated_keys_are_the_centred_keys_times_h_over_d", {})]),
+    ("e2m3_mantissa_step", "oracle.formats", "e2m3_decode", "np.ldexp(1.0 + m / 8.0", "np.ldexp(1.0 + m / 4.0",
+     [("test_oracle_mx6", "test_e2m3_value_table", {})]),
+    ("e2m3_tie_odd", "oracle.formats", "e2m3_encode", "(hi % 2 == 0)", "(hi % 2 == 1)",
+     [("test_oracle_mx6", "test_e2m3_encode_brute_force", {})]),
     # diagnostics
     ("cube_inner_first", "oracle.diagnostics", "static_cube_order", "np.lexsort((inner, cid))",
      "np.lexsort((cid, inner))", [("test_oracle_diagnostics", "test_static_cube_order_is_a_permutation_of_whole_cubes", {})]),
