@@ -30,7 +30,8 @@ __all__ = ["VCError", "lib", "vc_vsmooth_group", "vc_vsmooth_demean_quant", "vc_
            "VC_DQ_HADAMARD", "STATUS", "vc_workspace_size", "vc_validate_perm", "vc_test_quantize_q",
            "vc_test_attn_fwd_clock", "VC_OP_GROUP", "VC_OP_DEMEAN_QUANT", "VC_OP_DEMEAN_QUANT_MX4",
            "VC_OP_ATTN_FWD", "VC_OP_ATTN_FWD_MX4", "VC_OP_VALIDATE_PERM", "wall_clock_mhz",
-           "vc_vsmooth_group_static"]
+           "vc_vsmooth_group_static", "vc_vsmooth_demean_quant_mx6", "vc_attn_fwd_mx6", "vc_attention_mx6",
+           "vc_test_fp6_encode", "unpack_fp6", "pack_fp6", "VC_OP_DEMEAN_QUANT_MX6", "VC_OP_ATTN_FWD_MX6"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvcattn.so")
 
@@ -45,6 +46,8 @@ VC_OP_DEMEAN_QUANT_MX4 = 3
 VC_OP_ATTN_FWD = 4
 VC_OP_ATTN_FWD_MX4 = 5
 VC_OP_VALIDATE_PERM = 6
+VC_OP_DEMEAN_QUANT_MX6 = 7
+VC_OP_ATTN_FWD_MX6 = 8
 STATUS = {"VC_OK": 0, "VC_ERR_NULL": -1, "VC_ERR_SHAPE": -2, "VC_ERR_K": -3, "VC_ERR_ITERS": -4,
           "VC_ERR_WORKSPACE": -5, "VC_ERR_OVERFLOW": -6, "VC_ERR_FLAGS": -7, "VC_ERR_HIP": -8}
 
@@ -64,7 +67,10 @@ _SIGNATURES = {
     "vc_attn_fwd": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
     "vc_vsmooth_demean_quant_mx4": (_I, [_P, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _P, _P, _Z, _P]),
     "vc_attn_fwd_mx4": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
+    "vc_vsmooth_demean_quant_mx6": (_I, [_P, _P, _P, _I, _I, _I, _I, _U, _P, _P, _P, _P, _P, _P, _Z, _P]),
+    "vc_attn_fwd_mx6": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P]),
     "vc_test_fp4_encode": (_I, [_P, _P, _Z, _P]),
+    "vc_test_fp6_encode": (_I, [_P, _P, _P, _Z, _P]),
     "vc_test_mfma_fp8_rate": (_I, [_P, _I, _I, _P, _P]),
     "vc_test_expcast": (_I, [_P, _P, _Z, _P]),
     "vc_test_e4m3_encode": (_I, [_P, _P, _Z, _P]),
@@ -340,6 +346,99 @@ def vc_attn_fwd_mx4(Q: torch.Tensor, Kq4: torch.Tensor, sK4: torch.Tensor, Rq4: 
     _check(lib().vc_attn_fwd_mx4(_ptr(Q), _ptr(Kq4), _ptr(sK4), _ptr(Rq4), _ptr(sR4), _ptr(mu), B, H, N, d,
                                  float(softmax_scale), flags, _ptr(out), _stream()), "vc_attn_fwd_mx4")
     return out
+
+
+def vc_vsmooth_demean_quant_mx6(K: torch.Tensor, V: torch.Tensor, perm: Optional[torch.Tensor] = None,
+                                no_demean: bool = False, hadamard: bool = False):
+    """6-bit (MX E2M3, per-32 E8M0 scales, 32-byte groups) operands of the VC path."""
+    B, H, N, d = _bhnd(K, "K")
+    _need(V, "V", torch.bfloat16, (B, H, N, d))
+    if perm is not None:
+        _need(perm, "perm", torch.int32, (B, H, N))
+    dev = K.device
+    T = N // 128 if N % 128 == 0 else 0
+    Kq6 = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    sK6 = torch.empty((B, H, N, d // 32), dtype=torch.uint8, device=dev)
+    Rq6 = torch.empty((B, H, T, d, 128), dtype=torch.uint8, device=dev)
+    sR6 = torch.empty((B, H, T, d, 4), dtype=torch.uint8, device=dev)
+    mu = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+    nws = lib().vc_demean_quant_workspace_size(B, H, N)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    flags = (VC_DQ_NO_DEMEAN if no_demean else 0) | (VC_DQ_HADAMARD if hadamard else 0)
+    _check(lib().vc_vsmooth_demean_quant_mx6(_ptr(K), _ptr(V), _ptr(perm), B, H, N, d, flags, _ptr(Kq6),
+                                             _ptr(sK6), _ptr(Rq6), _ptr(sR6), _ptr(mu), _ptr(ws), nws, _stream()),
+           "vc_vsmooth_demean_quant_mx6")
+    return {"Kq6": Kq6, "sK6": sK6, "Rq6": Rq6, "sR6": sR6, "mu": mu}
+
+
+def vc_attn_fwd_mx6(Q: torch.Tensor, Kq6: torch.Tensor, sK6: torch.Tensor, Rq6: torch.Tensor,
+                    sR6: torch.Tensor, mu: Optional[torch.Tensor], softmax_scale: float = 0.0,
+                    no_mean: bool = False, hadamard: bool = False,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """6-bit attention: MX E2M3 Q, K, P and residual, P = 2^(S L4 - m), mean restore (Eq. 1, 6)."""
+    B, H, N, d = _bhnd(Q, "Q")
+    T = N // 128 if N % 128 == 0 else 0
+    _need(Kq6, "Kq6", torch.uint8, (B, H, N, d))
+    _need(sK6, "sK6", torch.uint8, (B, H, N, d // 32))
+    _need(Rq6, "Rq6", torch.uint8, (B, H, T, d, 128))
+    _need(sR6, "sR6", torch.uint8, (B, H, T, d, 4))
+    if mu is not None or not no_mean:
+        _need(mu, "mu", torch.bfloat16, (B, H, T, d))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=Q.device)
+    else:
+        _need(out, "out", torch.bfloat16, (B, H, N, d))
+    flags = (VC_ATTN_NO_MEAN if no_mean else 0) | (VC_ATTN_HADAMARD if hadamard else 0)
+    _check(lib().vc_attn_fwd_mx6(_ptr(Q), _ptr(Kq6), _ptr(sK6), _ptr(Rq6), _ptr(sR6), _ptr(mu), B, H, N, d,
+                                 float(softmax_scale), flags, _ptr(out), _stream()), "vc_attn_fwd_mx6")
+    return out
+
+
+def vc_attention_mx6(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool = False,
+                     hadamard: bool = False):
+    """6-bit demean_quant then 6-bit attention for a given pi."""
+    ops = vc_vsmooth_demean_quant_mx6(K, V, perm, no_demean=no_demean, hadamard=hadamard)
+    return vc_attn_fwd_mx6(Q, ops["Kq6"], ops["sK6"], ops["Rq6"], ops["sR6"], ops["mu"], softmax_scale,
+                           no_mean=no_demean, hadamard=hadamard)
+
+
+def vc_test_fp6_encode(x: torch.Tensor, scale: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Words 6i .. 6i+5 (int32) = E2M3 codes of x[32i .. 32i+31] (value k in bits 6k .. 6k+5),
+    converted with scale[i] as the conversion's scale operand when given."""
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous() or x.numel() % 32:
+        raise ValueError("x must be a contiguous float32 device tensor of a multiple of 32 values")
+    n = x.numel() // 32
+    if scale is not None:
+        _need(scale, "scale", torch.float32, (n,))
+    out = torch.empty(6 * n, dtype=torch.int32, device=x.device)
+    _check(lib().vc_test_fp6_encode(_ptr(x), _ptr(scale), _ptr(out), n, _stream()), "vc_test_fp6_encode")
+    return out
+
+
+def unpack_fp6(b) -> np.ndarray:
+    """uint8 [..., 32 g] (a tensor or array: groups of 32 bytes, 24 code bytes then 8 pad bytes, or
+    of 24 code bytes when the last axis is a multiple of 24 but not of 32) -> E2M3 codes uint8
+    [..., 32 g]: value k of a group in bits 6k .. 6k+5 of its 192-bit little-endian field."""
+    a = b.cpu().numpy() if isinstance(b, torch.Tensor) else np.asarray(b)
+    a = a.astype(np.uint8)
+    n = a.shape[-1]
+    g = a.reshape(a.shape[:-1] + (n // 32, 32))[..., :24] if n % 32 == 0 else a.reshape(a.shape[:-1] + (n // 24, 24))
+    bits = np.unpackbits(g, axis=-1, bitorder="little").reshape(g.shape[:-1] + (32, 6))
+    codes = (bits << np.arange(6, dtype=np.uint8)).sum(-1).astype(np.uint8)
+    return codes.reshape(g.shape[:-2] + (g.shape[-2] * 32,))
+
+
+def pack_fp6(codes) -> np.ndarray:
+    """E2M3 codes uint8 [..., 32 g] -> the 6-bit layout uint8 [..., 32 g] (per group of 32: 24 code
+    bytes, value k in bits 6k .. 6k+5, then 8 zero bytes)."""
+    c = codes.cpu().numpy() if isinstance(codes, torch.Tensor) else np.asarray(codes)
+    c = c.astype(np.uint8)
+    n = c.shape[-1]
+    g = c.reshape(c.shape[:-1] + (n // 32, 32))
+    bits = ((g[..., None] >> np.arange(6, dtype=np.uint8)) & 1).astype(np.uint8).reshape(g.shape[:-1] + (192,))
+    body = np.packbits(bits, axis=-1, bitorder="little")
+    out = np.concatenate([body, np.zeros(body.shape[:-1] + (8,), np.uint8)], axis=-1)
+    return out.reshape(c.shape)
 
 
 def vc_attention_mx4(Q, K, V, perm=None, softmax_scale: float = 0.0, no_demean: bool = False,

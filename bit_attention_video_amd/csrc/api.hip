@@ -168,12 +168,14 @@ size_t vc_workspace_size(int op, int B, int H, int N, int d, int k) {
   switch (op) {
     case VC_OP_GROUP: return vc_group_workspace_size(B, H, N, k);
     case VC_OP_DEMEAN_QUANT:
-    case VC_OP_DEMEAN_QUANT_MX4: return vc_demean_quant_workspace_size(B, H, N);
+    case VC_OP_DEMEAN_QUANT_MX4:
+    case VC_OP_DEMEAN_QUANT_MX6: return vc_demean_quant_workspace_size(B, H, N);
     case VC_OP_VALIDATE_PERM:
       if (B <= 0 || H <= 0 || N <= 0) return 0;
       return align256((size_t)B * H * (size_t)((N + 31) / 32) * sizeof(uint32_t));
     case VC_OP_ATTN_FWD:
-    case VC_OP_ATTN_FWD_MX4: return 0;
+    case VC_OP_ATTN_FWD_MX4:
+    case VC_OP_ATTN_FWD_MX6: return 0;
     default: return 0;
   }
 }
@@ -258,7 +260,45 @@ int vc_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4, c
   // L4 = float32(log2(e) * scale), the scale taken in double (1/sqrt(d) when 0 is passed)
   const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;
   const float L4 = (float)(1.4426950408889634 * scale);
-  return hip_status(vc_launch_attn_fwd_mx4(Q, Kq4, sK4, Rq4, sR4, mu, B * H, N, L4, flags, O, stream));
+  return hip_status(vc_launch_attn_fwd_mx4(Q, Kq4, sK4, Rq4, sR4, mu, B * H, N, L4, flags, O, 4, stream));
+}
+
+int vc_vsmooth_demean_quant_mx6(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                int B, int H, int N, int d, unsigned flags,
+                                uint8_t* Kq6, uint8_t* sK6, uint8_t* Rq6, uint8_t* sR6,
+                                uint16_t* mu_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!K || !V || !Kq6 || !sK6 || !Rq6 || !sR6 || !mu_out || !ws) return VC_ERR_NULL;
+  if (flags & ~(VC_DQ_NO_DEMEAN | VC_DQ_HADAMARD)) return VC_ERR_FLAGS;
+  int BH = B * H;
+  vc_dq_ws L = vc_dq_ws_layout(BH, N);
+  if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
+  return hip_status(vc_launch_demean_quant_mx6(K, V, perm, BH, N, flags, Kq6, sK6, Rq6, sR6, mu_out,
+                                               (char*)ws, L, stream));
+}
+
+int vc_attn_fwd_mx6(const uint16_t* Q, const uint8_t* Kq6, const uint8_t* sK6, const uint8_t* Rq6,
+                    const uint8_t* sR6, const uint16_t* mu, int B, int H, int N, int d,
+                    float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream) {
+  int st = check_shape(B, H, N, d);
+  if (st < 0) return st;
+  if (st == 1) return VC_OK;
+  if (!Q || !Kq6 || !sK6 || !Rq6 || !sR6 || !O) return VC_ERR_NULL;
+  if (!mu && !(flags & VC_ATTN_NO_MEAN)) return VC_ERR_NULL;
+  if (flags & ~(VC_ATTN_NO_MEAN | VC_ATTN_HADAMARD)) return VC_ERR_FLAGS;
+  if (!(softmax_scale >= 0.0f) || isinf(softmax_scale)) return VC_ERR_SHAPE;
+  const double scale = softmax_scale == 0.0f ? 1.0 / sqrt((double)d) : (double)softmax_scale;
+  const float L4 = (float)(1.4426950408889634 * scale);
+  return hip_status(vc_launch_attn_fwd_mx4(Q, Kq6, sK6, Rq6, sR6, mu, B * H, N, L4, flags, O, 6, stream));
+}
+
+int vc_test_fp6_encode(const float* x, const float* scale, uint32_t* words, size_t ngroups, hipStream_t stream) {
+  if (ngroups == 0) return VC_OK;
+  if (!x || !words) return VC_ERR_NULL;
+  if (ngroups >= (size_t(1) << 35)) return VC_ERR_OVERFLOW;
+  return hip_status(vc_launch_test_fp6(x, scale, words, ngroups, stream));
 }
 
 int vc_test_fp4_encode(const float* x, uint8_t* codes, size_t n, hipStream_t stream) {

@@ -22,6 +22,10 @@
 //    returns t = S L4 - m directly; alpha = 2^(-delta);
 //  * means are stored unscaled (App. B: the microscales act inside the instruction) and
 //    O = bf16(A / l).
+// The same kernel runs the 6-bit path (BITS = 6, MX E2M3 elements): a row of a tile is then
+// four 32-byte groups (24 code bytes, 8 zero bytes), i.e. 128-byte rows swizzled like the
+// 8-bit kernel's, a lane's fragment is the 24 code bytes of its group (six registers), and the
+// conversions are the E2M3 ones (scale rule: amax <= 7.5 2^E).
 #include "vc_common.h"
 #include "vc_internal.h"
 #include "vc_attn.h"
@@ -35,8 +39,20 @@ using namespace vc_attn;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 
-constexpr int TILE4 = 128 * 64;     // E2M1 bytes of a 128 x 128 tile
-constexpr int STILE = 128 * 4;      // its scale bytes
+typedef int v6i_ __attribute__((ext_vector_type(6)));
+
+// Element formats: bytes per tile row, the matrix instructions' format code, 16-byte copies per
+// lane and wave for one tile, the register type of a lane's 32 elements.
+template <int BITS> struct MxFmt;
+template <> struct MxFmt<4> {
+  static constexpr int ROWB = 64, CODE = 4, NCOPY = 1;
+  typedef v4i frag_t;
+};
+template <> struct MxFmt<6> {
+  static constexpr int ROWB = 128, CODE = 2, NCOPY = 2;
+  typedef v6i_ frag_t;
+};
+constexpr int STILE = 128 * 4;      // scale bytes of a tile
 constexpr int NWAVE = 8;
 constexpr int MRING = 32;
 constexpr int NBUF = 4;
@@ -60,17 +76,51 @@ __device__ __forceinline__ v4i lds_frag16(const uint8_t* tile, int row, int c) {
   return v4i{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
 }
 
+// 6-bit tiles: 128-byte rows, 16-byte chunk c16 (0..7) of row `row` XOR-swizzled by
+// (row % 8) ^ (row / 8 % 2) as in the 8-bit kernel; group g is chunks 2 g and 2 g + 1.
+__device__ __forceinline__ int swz6(int row, int c16) {
+  return row * 128 + ((c16 ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
+// Source offset of the chunk lane `lane` of wave w copies with instruction i: the instruction
+// fills LDS chunks (2 w + i) * 64 + lane of the swizzled tile.
+__device__ __forceinline__ int stage6_src(int w, int i, int lane) {
+  const int P = (2 * w + i) * 64 + lane;
+  const int row = P >> 3;
+  return row * 128 + (((P & 7) ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+}
+// The 24 code bytes of group g of row `row`: all of chunk 2 g and the first half of 2 g + 1.
+__device__ __forceinline__ v6i_ lds_frag24(const uint8_t* tile, int row, int g) {
+  const uint4 lo = *(const uint4*)(tile + swz6(row, 2 * g));
+  const uint2 hi = *(const uint2*)(tile + swz6(row, 2 * g + 1));
+  return v6i_{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y};
+}
+
+template <int BITS>
+__device__ __forceinline__ typename MxFmt<BITS>::frag_t lds_frag(const uint8_t* tile, int row, int g) {
+  if constexpr (BITS == 4) return lds_frag16(tile, row, g);
+  else return lds_frag24(tile, row, g);
+}
+template <int BITS>
+__device__ __forceinline__ int stage_src_mx(int w, int i, int lane) {
+  if constexpr (BITS == 4) return stage4_src(w, lane);
+  else return stage6_src(w, i, lane);
+}
+
+// The instructions take eight registers; only the first four (E2M1) or six (E2M3) are read.
 __device__ __forceinline__ v8i wide(v4i a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3, 0, 1, 2, 3); }
+__device__ __forceinline__ v8i wide(v6i_ a) { return __builtin_shufflevector(a, a, 0, 1, 2, 3, 4, 5, 0, 1); }
 
 // E2M1 x E2M1 -> float32; byte OA of sa and byte OB of sb are the E8M0 scales of this lane's
 // A and B groups.
-template <int OA, int OB>
-__device__ __forceinline__ v16f mfma_fp4(v4i a, v4i b, v16f c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(a), wide(b), c, 4, 4, OA, sa, OB, sb);
+template <int BITS, int OA, int OB, typename F>
+__device__ __forceinline__ v16f mfma_mx(F a, F b, v16f c, int sa, int sb) {
+  constexpr int C = MxFmt<BITS>::CODE;
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wide(a), wide(b), c, C, C, OA, sa, OB, sb);
 }
-template <int OB>
-__device__ __forceinline__ v4f mfma_fp4_16(v4i a, v4i b, v4f c, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wide(a), wide(b), c, 4, 4, 0, 127, OB, sb);
+template <int BITS, int OB, typename F>
+__device__ __forceinline__ v4f mfma_mx_16(F a, F b, v4f c, int sb) {
+  constexpr int C = MxFmt<BITS>::CODE;
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wide(a), wide(b), c, C, C, 0, 127, OB, sb);
 }
 
 // Constant A operand of the row-sum product (16x16x128, E2M1): the same 0/1 pattern as the
@@ -90,6 +140,22 @@ __device__ __forceinline__ v4i rowsum_ones4(int lane) {
   asm volatile("" : "+v"(r));
   return r;
 }
+// The same operand in E2M3, built by the conversion itself (32 ones or 32 zeros), so its bit
+// layout is the one the instruction reads.
+__device__ __forceinline__ v6i_ rowsum_ones6(int lane) {
+  const float one = rowsum_ones4_word(lane) ? 1.0f : 0.0f;
+  float x[32];
+#pragma unroll
+  for (int k = 0; k < 32; ++k) x[k] = one;
+  v6i_ r = fp6x32(x);
+  asm volatile("" : "+v"(r));
+  return r;
+}
+template <int BITS>
+__device__ __forceinline__ typename MxFmt<BITS>::frag_t rowsum_ones_mx(int lane) {
+  if constexpr (BITS == 4) return rowsum_ones4(lane);
+  else return rowsum_ones6(lane);
+}
 
 // E2M1 codes of 32 values x divided by their power-of-two group scale `scale`: nibble k = value
 // k.  The conversion instruction divides by its scale operand itself (bit for bit the codes of
@@ -107,8 +173,30 @@ __device__ __forceinline__ v4i pack_fp4_32(const float* x, float scale) {
   }
   return r;
 }
+// E2M3 codes of 32 values divided by their group scale (the conversion divides by its scale
+// operand; checked on the device for power-of-two scales), value k in bits 6k .. 6k + 5: the
+// conversion interleaves its two operands, so the even values go in the first (as fp6x32).
+__device__ __forceinline__ v6i_ pack_fp6_32(const float* x, float scale) {
+  v16f lo, hi;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    lo[k] = x[2 * k];
+    hi[k] = x[2 * k + 1];
+  }
+  return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, scale);
+}
+template <int BITS>
+__device__ __forceinline__ typename MxFmt<BITS>::frag_t pack_mx(const float* x, float scale) {
+  if constexpr (BITS == 4) return pack_fp4_32(x, scale);
+  else return pack_fp6_32(x, scale);
+}
+template <int BITS>
+__device__ __forceinline__ int mx_exp(float amax) {
+  if constexpr (BITS == 4) return mx_exponent(amax);
+  else return mx6_exponent(amax);
+}
 
-template <bool NO_MEAN, bool HAD>
+template <int BITS, bool NO_MEAN, bool HAD>
 __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict__ Q,
                                                       const uint8_t* __restrict__ Kq4,
                                                       const uint8_t* __restrict__ sK4,
@@ -117,6 +205,9 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
                                                       const uint16_t* __restrict__ mu, int N, int nqb,
                                                       int nwb, uint32_t G, float L4,
                                                       uint16_t* __restrict__ O) {
+  using FM = MxFmt<BITS>;
+  typedef typename FM::frag_t frag_t;
+  constexpr int TILE4 = 128 * FM::ROWB;    // code bytes of a 128 x 128 tile
   __shared__ __attribute__((aligned(1024))) uint8_t kt[NBUF][TILE4];
   __shared__ __attribute__((aligned(1024))) uint8_t rt[NBUF][TILE4];
   __shared__ __attribute__((aligned(256))) uint8_t kst[NBUF][STILE];
@@ -133,26 +224,30 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   const int T = N / 128;
   const size_t headN = (size_t)bh * N;
   const int qi = (valid ? qb : nqb - 1) * 128 + (w & 3) * 32 + q;
-  const uint8_t* Kh = Kq4 + headN * (VC_D / 2);
+  const uint8_t* Kh = Kq4 + headN * FM::ROWB;
   const uint8_t* sKh = sK4 + headN * 4;
   const uint8_t* Rh = Rq4 + (size_t)bh * T * TILE4;
   const uint8_t* sRh = sR4 + (size_t)bh * T * STILE;
   const uint16_t* muh = mu + (size_t)bh * T * VC_D;
 
-  // copies per wave and step: one 16-byte chunk per lane of the K and of the R code tile; waves
-  // 0-1 copy the K scale tile, waves 2-3 the R scale tile (4 bytes per lane), wave 4 the mean row
-  const uint32_t so = stage4_src(w, lane);
-  const uint32_t kt0 = lds_addr(&kt[0][0]) + w * 1024, rt0 = lds_addr(&rt[0][0]) + w * 1024;
+  // copies per wave and step: NCOPY 16-byte chunks per lane of the K and of the R code tile;
+  // waves 0-1 copy the K scale tile, waves 2-3 the R scale tile (4 bytes per lane), wave 4 the
+  // mean row
+  constexpr int NC = FM::NCOPY;
+  const uint32_t so = stage_src_mx<BITS>(w, 0, lane), so1 = stage_src_mx<BITS>(w, NC - 1, lane);
+  const uint32_t kt0 = lds_addr(&kt[0][0]) + NC * w * 1024, rt0 = lds_addr(&rt[0][0]) + NC * w * 1024;
   const uint32_t ks0 = lds_addr(&kst[0][0]), rs0 = lds_addr(&rst[0][0]);
   const uint32_t mr0 = lds_addr(&mring[0][0]);
   constexpr int D = NBUF - 1;
   auto clampT = [&](int i) { return i < T ? i : T - 1; };
   auto k_tile = [&](int i, int slot) {
     dma16(Kh + (size_t)i * TILE4, so, kt0 + slot * TILE4);
+    if constexpr (NC == 2) dma16(Kh + (size_t)i * TILE4, so1, kt0 + slot * TILE4 + 1024);
     if (w < 2) dma4(sKh + (size_t)i * STILE + 256 * w, 4 * lane, ks0 + slot * STILE + 256 * w);
   };
   auto r_tile = [&](int i, int slot) {
     dma16(Rh + (size_t)i * TILE4, so, rt0 + slot * TILE4);
+    if constexpr (NC == 2) dma16(Rh + (size_t)i * TILE4, so1, rt0 + slot * TILE4 + 1024);
     if (w == 2 || w == 3) dma4(sRh + (size_t)i * STILE + 256 * (w - 2), 4 * lane, rs0 + slot * STILE + 256 * (w - 2));
     if (!NO_MEAN && w == 4) dma4(muh + (size_t)i * VC_D, 4 * lane, mr0 + (i % MRING) * 256);
   };
@@ -162,8 +257,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   };
   const bool extra = w < 4 || (!NO_MEAN && w == 4);   // this wave issues a third copy per step
   auto wait_step = [&]() {
-    if (extra) wait_dma_barrier<(D - 2) * 3>();
-    else wait_dma_barrier<(D - 2) * 2>();
+    if (extra) wait_dma_barrier<(D - 2) * (2 * NC + 1)>();
+    else wait_dma_barrier<(D - 2) * 2 * NC>();
   };
 
   if (!NO_MEAN)
@@ -192,20 +287,20 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
       }
     }
   if constexpr (HAD) hadamard_q_row(qs, hl);
-  v4i qf[2];
+  frag_t qf[2];
   int qsc = 0;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     float a = 0.0f;
 #pragma unroll
     for (int k = 0; k < 32; ++k) a = fmaxf(a, fabsf(qs[32 * c + k]));
-    const int E = mx_exponent(a);
-    qf[c] = pack_fp4_32(&qs[32 * c], __builtin_ldexpf(1.0f, E));
+    const int E = mx_exp<BITS>(a);
+    qf[c] = pack_mx<BITS>(&qs[32 * c], __builtin_ldexpf(1.0f, E));
     qsc |= (E + 127) << (8 * c);
   }
   wait_dma_barrier<0>();
 
-  const v4i ones = rowsum_ones4(lane);
+  const frag_t ones = rowsum_ones_mx<BITS>(lane);
   float b = 0.0f, l_run = 0.0f;   // b = -m
   // b in every element: the QK accumulator input, kept in registers and rebuilt only when b
   // changes (a running-maximum update)
@@ -234,11 +329,11 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   v16f s[4];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) s[kb] = v16f{};
-  v4i pw[2] = {};
+  frag_t pw[2] = {};
   int psc = 0x7F7F;               // P scales of the two PV steps (bytes 0 and 1)
-  v4i rf[8];                      // residual fragments of the next PV product
+  frag_t rf[8];                   // residual fragments of the next PV product
 #pragma unroll
-  for (int i = 0; i < 8; ++i) rf[i] = v4i{};
+  for (int i = 0; i < 8; ++i) rf[i] = frag_t{};
   // their scale dwords shifted right by 8 h: bytes 0 and 2 are then the groups h and 2 + h of
   // this lane half's 32-slot blocks in the two PV steps
   int rsw[4] = {0, 0, 0, 0};
@@ -285,32 +380,32 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   // M(j): A += P R and the row sum of tile j-1, then S^T of tile j (t = S L4 + b).
   auto mphase = [&](int j, auto qk, auto pv) {
     constexpr bool QK = decltype(qk)::value, PV = decltype(pv)::value;
-    v4i kf[8];
+    frag_t kf[8];
     int ksw[4];
     if constexpr (QK) {
       const uint8_t* kb_ = kt[j % NBUF];
       const uint8_t* ksb = kst[j % NBUF];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        kf[2 * kb] = lds_frag16(kb_, 32 * kb + q, hl);
-        kf[2 * kb + 1] = lds_frag16(kb_, 32 * kb + q, 2 + hl);
+        kf[2 * kb] = lds_frag<BITS>(kb_, 32 * kb + q, hl);
+        kf[2 * kb + 1] = lds_frag<BITS>(kb_, 32 * kb + q, 2 + hl);
         ksw[kb] = (int)(*(const uint32_t*)(ksb + 4 * (32 * kb + q)) >> (8 * hl));
       }
     }
     if constexpr (PV) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        acc[db] = mfma_fp4<0, 0>(rf[db], pw[0], acc[db], rsw[db], psc);
-        acc[db] = mfma_fp4<2, 1>(rf[4 + db], pw[1], acc[db], rsw[db], psc);
+        acc[db] = mfma_mx<BITS, 0, 0>(rf[db], pw[0], acc[db], rsw[db], psc);
+        acc[db] = mfma_mx<BITS, 2, 1>(rf[4 + db], pw[1], acc[db], rsw[db], psc);
       }
-      rs = mfma_fp4_16<0>(ones, pw[0], v4f{}, psc);
-      rs = mfma_fp4_16<1>(ones, pw[1], rs, psc);
+      rs = mfma_mx_16<BITS, 0>(ones, pw[0], v4f{}, psc);
+      rs = mfma_mx_16<BITS, 1>(ones, pw[1], rs, psc);
     }
     if constexpr (QK) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        s[kb] = mfma_fp4<0, 0>(kf[2 * kb], qf[0], bsplat, ksw[kb], qsc);
-        s[kb] = mfma_fp4<2, 1>(kf[2 * kb + 1], qf[1], s[kb], ksw[kb], qsc);
+        s[kb] = mfma_mx<BITS, 0, 0>(kf[2 * kb], qf[0], bsplat, ksw[kb], qsc);
+        s[kb] = mfma_mx<BITS, 2, 1>(kf[2 * kb + 1], qf[1], s[kb], ksw[kb], qsc);
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) keep(s[kb]);
@@ -375,8 +470,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
       // maximum did not grow) is the very float32 its exponential came from, so one more
       // exp2 returns that element's value (exp2 is monotonic) instead of a 32-value max
       const float a = __builtin_amdgcn_exp2f(gmax[p] - delta);
-      const int E = mx_exponent(a);
-      pw[p] = pack_fp4_32(e, __builtin_ldexpf(1.0f, E));
+      const int E = mx_exp<BITS>(a);
+      pw[p] = pack_mx<BITS>(e, __builtin_ldexpf(1.0f, E));
       sc |= (E + 127) << (8 * p);
     }
     psc = sc;
@@ -388,8 +483,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
       const uint8_t* rsb = rst[j % NBUF];
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        rf[db] = lds_frag16(rb, 32 * db + q, hl);
-        rf[4 + db] = lds_frag16(rb, 32 * db + q, 2 + hl);
+        rf[db] = lds_frag<BITS>(rb, 32 * db + q, hl);
+        rf[4 + db] = lds_frag<BITS>(rb, 32 * db + q, 2 + hl);
         rsw[db] = (int)(*(const uint32_t*)(rsb + 4 * (32 * db + q)) >> (8 * hl));
       }
     }
@@ -468,16 +563,23 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
 hipError_t vc_launch_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4,
                                   const uint8_t* Rq4, const uint8_t* sR4, const uint16_t* mu,
                                   int BH, int N, float L4, unsigned flags, uint16_t* O,
-                                  hipStream_t s) {
+                                  int bits, hipStream_t s) {
   const int nqb = N / 128, nwb = (nqb + 1) / 2;
   const uint32_t G = (uint32_t)BH * (uint32_t)nwb;
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(G), dim3(NWAVE * 64), 0, s, Q, Kq4, sK4, Rq4, sR4, mu, N, nqb, nwb, G, L4, O);
   };
   const bool no_mean = flags & VC_ATTN_NO_MEAN, had = flags & VC_ATTN_HADAMARD;
-  if (no_mean && had) launch(k_attn_fwd_mx4<true, true>);
-  else if (no_mean) launch(k_attn_fwd_mx4<true, false>);
-  else if (had) launch(k_attn_fwd_mx4<false, true>);
-  else launch(k_attn_fwd_mx4<false, false>);
+  if (bits == 6) {
+    if (no_mean && had) launch(k_attn_fwd_mx4<6, true, true>);
+    else if (no_mean) launch(k_attn_fwd_mx4<6, true, false>);
+    else if (had) launch(k_attn_fwd_mx4<6, false, true>);
+    else launch(k_attn_fwd_mx4<6, false, false>);
+  } else {
+    if (no_mean && had) launch(k_attn_fwd_mx4<4, true, true>);
+    else if (no_mean) launch(k_attn_fwd_mx4<4, true, false>);
+    else if (had) launch(k_attn_fwd_mx4<4, false, true>);
+    else launch(k_attn_fwd_mx4<4, false, false>);
+  }
   return hipGetLastError();
 }

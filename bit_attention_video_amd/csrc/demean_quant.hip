@@ -19,6 +19,8 @@
 //   k_vpass2         sV = (maximum of the eight) / 448; codes of R / sV into the tile-transposed
 //                    PV operand order;
 //                    mu~ = bf16(mu / sV)
+//   k_kquant4, k_vquant4   the 4-bit path's K and V operands (MX E2M1, per-32 scales)
+//   k_kquant6, k_vquant6   the 6-bit path's (MX E2M3, per-32 scales, 32-byte groups)
 #include "vc_common.h"
 #include "vc_internal.h"
 #include "vc_attn.h"
@@ -176,15 +178,28 @@ __device__ __forceinline__ double dpp_quad_xor(double v, int m) {
   return __builtin_bit_cast(double, ((uint64_t)(uint32_t)rhi << 32) | (uint32_t)rlo);
 }
 
-__global__ __launch_bounds__(512) void k_kquant_had(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
-                                                    const float* __restrict__ kbar, int N,
-                                                    uint8_t* __restrict__ Kq, float* __restrict__ sK) {
-  __shared__ float red8[8];
-  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
-  const int row = t >> 2, c4 = t & 3;
-  const int tok = dq_token(perm, bh, N, j * VC_BLK + row);
-  const uint4* src = (const uint4*)(K + ((size_t)bh * N + tok) * VC_D + 32 * c4);
-  const float* kb = kbar + (size_t)bh * VC_D + 32 * c4;
+// One quarter of a permuted row, channels 32 c4 .. 32 c4 + 31, centred: z = float32(K - kbar).
+// With HAD, the quad's four lanes then rotate their row by H (float64 butterflies, as above)
+// and z is float32 of the exact rotated value.
+template <bool HAD>
+__device__ __forceinline__ void centred_quarter_row(const uint16_t* __restrict__ krow, const float* __restrict__ kb,
+                                                    int c4, float* z) {
+  const uint4* src = (const uint4*)(krow + 32 * c4);
+  if constexpr (!HAD) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const uint4 raw = src[v];
+      const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+      const float4 k0 = *(const float4*)(kb + 8 * v), k1 = *(const float4*)(kb + 8 * v + 4);
+      const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[8 * v + 2 * e] = bf16_to_f32(wd[e] & 0xFFFFu) - kk[2 * e];
+        z[8 * v + 2 * e + 1] = bf16_to_f32(wd[e] >> 16) - kk[2 * e + 1];
+      }
+    }
+    return;
+  }
   double y[32];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -216,13 +231,22 @@ __global__ __launch_bounds__(512) void k_kquant_had(const uint16_t* __restrict__
       y[k] = upper ? o - y[k] : y[k] + o;
     }
   }
+#pragma unroll
+  for (int k = 0; k < 32; ++k) z[k] = (float)y[k];
+}
+
+__global__ __launch_bounds__(512) void k_kquant_had(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
+                                                    const float* __restrict__ kbar, int N,
+                                                    uint8_t* __restrict__ Kq, float* __restrict__ sK) {
+  __shared__ float red8[8];
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int row = t >> 2, c4 = t & 3;
+  const int tok = dq_token(perm, bh, N, j * VC_BLK + row);
   float z[32];
+  centred_quarter_row<true>(K + ((size_t)bh * N + tok) * VC_D, kbar + (size_t)bh * VC_D + 32 * c4, c4, z);
   float amax = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    z[k] = (float)y[k];
-    amax = fmaxf(amax, fabsf(z[k]));
-  }
+  for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(z[k]));
   amax = block_max_512(amax, red8);
   const int E = pow2_block_exponent(amax);
   const float inv = __builtin_ldexpf(1.0f, -E);   // exact: the scale is a power of two
@@ -493,6 +517,116 @@ __global__ __launch_bounds__(256) void k_vquant4(const uint16_t* __restrict__ V,
     *(uint4*)(dst + 16 * c) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   }
   if (t < VC_D) ((uint32_t*)(sR4 + ((size_t)bh * nt + j) * (VC_D * 4)))[t] = ((const uint32_t*)stile)[t];
+}
+
+// 6-bit K (MX E2M3): four lanes per permuted row, lane (row, c4) quantising channels
+// 32 c4 .. 32 c4 + 31, one scale group: its own maximum, E = mx6_exponent, codes of z / 2^E
+// (exact division) packed into 24 bytes, then 8 zero bytes, so a row is four 32-byte groups
+// (the layout the 6-bit attention's fragments read).  With HAD the row is rotated first and the
+// stored exponent lowered by 7 (the 1/128 of H / 128).
+template <bool HAD>
+__global__ __launch_bounds__(512) void k_kquant6(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
+                                                 const float* __restrict__ kbar, int N,
+                                                 uint8_t* __restrict__ Kq6, uint8_t* __restrict__ sK6) {
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int row = t >> 2, c4 = t & 3;
+  const int tok = dq_token(perm, bh, N, j * VC_BLK + row);
+  float z[32];
+  centred_quarter_row<HAD>(K + ((size_t)bh * N + tok) * VC_D, kbar + (size_t)bh * VC_D + 32 * c4, c4, z);
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(z[k]));
+  const int E = mx6_exponent(amax);
+  const float inv = __builtin_ldexpf(1.0f, -E);   // exact
+#pragma unroll
+  for (int k = 0; k < 32; ++k) z[k] *= inv;
+  const v6i w = fp6x32(z);
+  const size_t r = (size_t)bh * N + j * VC_BLK + row;
+  uint4* dst = (uint4*)(Kq6 + r * VC_D + 32 * c4);
+  dst[0] = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
+  dst[1] = make_uint4((uint32_t)w[4], (uint32_t)w[5], 0u, 0u);
+  sK6[r * 4 + c4] = (uint8_t)(E - (HAD ? 7 : 0) + 127);
+}
+
+// Slot of permuted row r (0..127) of a tile in the PV operand order: row 64 p + 32 hi + 8 mid
+// + 4 g + lo sits in slot 64 p + 32 g + 16 hi + 4 mid + lo.
+__device__ __forceinline__ int pv_slot(int r) {
+  return (r & 64) + 32 * ((r >> 2) & 1) + 16 * ((r >> 5) & 1) + 4 * ((r >> 3) & 3) + (r & 3);
+}
+
+// 6-bit V residual (MX E2M3), per tile j: R = V'[pi] - mu_j staged in LDS in slot order
+// [slot][channel] (float32; a thread writes four consecutive channels of one row), then
+// thread (channel, group) takes the 32 slots of its group, its maximum and scale, and writes
+// its 24 code bytes and 8 zero bytes to [channel][32 g] of the tile-transposed operand; scale
+// bytes [channel][group]; mu_out = bf16(mu_j), unscaled.
+__global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
+                                                 int N, const float* __restrict__ mu,
+                                                 uint8_t* __restrict__ Rq6, uint8_t* __restrict__ sR6,
+                                                 uint16_t* __restrict__ mu_out) {
+  __shared__ float mus[VC_D];
+  __shared__ __attribute__((aligned(16))) float rs[VC_BLK * VC_D];
+  const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
+  const int q4 = t & 31, rg = t >> 5;
+  const int nt = N / VC_BLK;
+  const size_t tile = (size_t)bh * nt + j;
+  if (t < VC_D) {
+    const float m = mu[tile * VC_D + t];
+    mus[t] = m;
+    mu_out[tile * VC_D + t] = (uint16_t)f32_to_bf16_rne(m);
+  }
+  __syncthreads();
+  const float4 m4 = *(const float4*)(mus + 4 * q4);
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int r = rg + 8 * i;
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + r);
+    float v[4];
+    load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
+    *(float4*)(rs + pv_slot(r) * VC_D + 4 * q4) = make_float4(v[0] - m4.x, v[1] - m4.y, v[2] - m4.z, v[3] - m4.w);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int pidx = t + 256 * k, ch = pidx & (VC_D - 1), g = pidx >> 7;
+    float x[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      x[i] = rs[(32 * g + i) * VC_D + ch];
+      amax = fmaxf(amax, fabsf(x[i]));
+    }
+    const int E = mx6_exponent(amax);
+    const float inv = __builtin_ldexpf(1.0f, -E);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] *= inv;
+    const v6i w = fp6x32(x);
+    uint4* dst = (uint4*)(Rq6 + (tile * VC_D + ch) * VC_BLK + 32 * g);
+    dst[0] = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
+    dst[1] = make_uint4((uint32_t)w[4], (uint32_t)w[5], 0u, 0u);
+    sR6[(tile * VC_D + ch) * 4 + g] = (uint8_t)(E + 127);
+  }
+}
+
+hipError_t vc_launch_demean_quant_mx6(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                      int BH, int N, unsigned flags, uint8_t* Kq6, uint8_t* sK6,
+                                      uint8_t* Rq6, uint8_t* sR6, uint16_t* mu_out, char* ws,
+                                      const vc_dq_ws& L, hipStream_t s) {
+  const int nchunk = (N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  const int nt = N / VC_BLK;
+  double* kpart = (double*)(ws + L.kpart);
+  float* kbar = (float*)(ws + L.kbar);
+  float* mu = (float*)(ws + L.mu);
+  float* amaxp = (float*)(ws + L.amaxp);
+  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
+  hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
+  if (flags & VC_DQ_HADAMARD)
+    hipLaunchKernelGGL(k_kquant6<true>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq6, sK6);
+  else
+    hipLaunchKernelGGL(k_kquant6<false>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq6, sK6);
+  hipLaunchKernelGGL(k_vpass1, dim3(nt, BH), dim3(512), 0, s, V, perm, N,
+                     (flags & VC_DQ_NO_DEMEAN) ? 0 : 1, mu, amaxp);
+  hipLaunchKernelGGL(k_vquant6, dim3(nt, BH), dim3(256), 0, s, V, perm, N, (const float*)mu, Rq6, sR6, mu_out);
+  return hipGetLastError();
 }
 
 hipError_t vc_launch_demean_quant_mx4(const uint16_t* K, const uint16_t* V, const int32_t* perm,

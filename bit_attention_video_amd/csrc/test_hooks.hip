@@ -1,5 +1,5 @@
 // Single-stage kernels exposed for testing: the ExpCast code (Sec. 3.3, Eq. 7), the E4M3
-// quantiser and the E2M1 conversion of the 4-bit path, each with the exact instruction
+// quantiser, the E2M1 conversion of the 4-bit path and the E2M3 conversion of the 6-bit path, each with the exact instruction
 // sequence the production kernels use; and a dense FP8 matrix-instruction loop that measures
 // the attainable FP8 rate of the device the attention kernel is compared against.
 #include "vc_common.h"
@@ -23,6 +23,27 @@ __global__ void k_test_e4m3(const float* __restrict__ x, uint8_t* __restrict__ c
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   size_t stride = (size_t)gridDim.x * blockDim.x;
   for (; i < n; i += stride) codes[i] = (uint8_t)(e4m3x2(x[i], 0.0f) & 0xFFu);
+}
+
+// Words 6i .. 6i+5 = the E2M3 codes of x[32i .. 32i+31] packed as the 6-bit paths pack them,
+// converted with the group's scale operand (scale[i], 1 when scale is null): the instruction
+// divides by it, as the 6-bit attention's P conversion relies on.
+__global__ void k_test_fp6(const float* __restrict__ x, const float* __restrict__ scale,
+                           uint32_t* __restrict__ words, size_t ngroups) {
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (; i < ngroups; i += stride) {
+    v16f lo, hi;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      lo[k] = x[32 * i + 2 * k];
+      hi[k] = x[32 * i + 2 * k + 1];
+    }
+    const float sc = scale ? scale[i] : 1.0f;
+    const v6i w = scale ? __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, sc) : fp6x32(&x[32 * i]);
+#pragma unroll
+    for (int k = 0; k < 6; ++k) words[6 * i + k] = (uint32_t)w[k];
+  }
 }
 
 // Byte i = E2M1 codes of the pair (x[2i], x[2i+1]) as the 4-bit quantisers pack them.
@@ -89,6 +110,11 @@ hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipS
 
 hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s) {
   hipLaunchKernelGGL(k_test_e4m3, dim3(grid_for(n)), dim3(256), 0, s, x, codes, n);
+  return hipGetLastError();
+}
+
+hipError_t vc_launch_test_fp6(const float* x, const float* scale, uint32_t* words, size_t ngroups, hipStream_t s) {
+  hipLaunchKernelGGL(k_test_fp6, dim3(grid_for(ngroups)), dim3(256), 0, s, x, scale, words, ngroups);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 #define VC_BLK 128
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v6i __attribute__((ext_vector_type(6)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
@@ -83,6 +84,32 @@ __device__ __forceinline__ int mx_exponent(float amax) {
   int e;
   const float m = __builtin_frexpf(amax, &e);
   const int E = m <= 0.75f ? e - 3 : e - 2;
+  return E < -100 ? -100 : E;
+}
+
+// E2M3 (OCP MX FP6) codes of the 32 values x[0..31], which the caller has already divided by
+// their power-of-two group scale (|x| <= 7.5): the hardware round-to-nearest-even conversion
+// with unit scale into six dwords, value k in bits 6k .. 6k + 5 of the 192 bits.  The
+// instruction interleaves its two 16-value operands (field 2i from the first, 2i + 1 from the
+// second; a layout probe on the device showed it), so the even values go in the first.
+__device__ __forceinline__ v6i fp6x32(const float* x) {
+  v16f lo, hi;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    lo[k] = x[2 * k];
+    hi[k] = x[2 * k + 1];
+  }
+  return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, 1.0f);
+}
+
+// Exponent E of an MX group scale for E2M3 elements: the smallest power of two 2^E with
+// amax <= 7.5 * 2^E (0 when amax == 0, never below -100).  With amax = m 2^e, m in [0.5, 1):
+// 7.5 * 2^(e-3) = 0.9375 * 2^e fits iff m <= 0.9375, and 7.5 * 2^(e-4) < 2^(e-1) never does.
+__device__ __forceinline__ int mx6_exponent(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  int e;
+  const float m = __builtin_frexpf(amax, &e);
+  const int E = m <= 0.9375f ? e - 3 : e - 2;
   return E < -100 ? -100 : E;
 }
 

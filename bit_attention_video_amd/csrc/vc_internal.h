@@ -35,6 +35,7 @@ constexpr int VC_KSTAT_CHUNK = 1024; // rows per key-mean partial
 hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t s);
 hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s);
 hipError_t vc_launch_test_fp4(const float* x, uint8_t* codes, size_t npair, hipStream_t s);
+hipError_t vc_launch_test_fp6(const float* x, const float* scale, uint32_t* words, size_t ngroups, hipStream_t s);
 hipError_t vc_launch_test_mfma_fp8_rate(float* out, int workgroups, int iters, float* clock_mhz,
                                         hipStream_t s);
 
@@ -54,15 +55,21 @@ hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const in
                                   uint8_t* Rq, uint16_t* mu_out, float* sV, char* ws,
                                   const vc_dq_ws& L, hipStream_t s);
 
+hipError_t vc_launch_demean_quant_mx6(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                      int BH, int N, unsigned flags, uint8_t* Kq6, uint8_t* sK6,
+                                      uint8_t* Rq6, uint8_t* sR6, uint16_t* mu_out, char* ws,
+                                      const vc_dq_ws& L, hipStream_t s);
+
 hipError_t vc_launch_demean_quant_mx4(const uint16_t* K, const uint16_t* V, const int32_t* perm,
                                       int BH, int N, unsigned flags, uint8_t* Kq4, uint8_t* sK4,
                                       uint8_t* Rq4, uint8_t* sR4, uint16_t* mu_out, char* ws,
                                       const vc_dq_ws& L, hipStream_t s);
 
+// bits = 4 (E2M1 operands, 64-byte rows) or 6 (E2M3 operands, 128-byte rows of 32-byte groups)
 hipError_t vc_launch_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4,
                                   const uint8_t* Rq4, const uint8_t* sR4, const uint16_t* mu,
                                   int BH, int N, float L4, unsigned flags, uint16_t* O,
-                                  hipStream_t s);  // L4 = float32(log2(e) softmax_scale)
+                                  int bits, hipStream_t s);  // L4 = float32(log2(e) softmax_scale)
 
 // clk: NULL, or 4 x vc_attn_fwd_workgroups(BH, N) uint64 that receive each workgroup's start
 // and end stamps (shader cycles, constant-rate ticks) for the clock probe.

@@ -66,6 +66,8 @@ enum vc_status {
 #define VC_OP_ATTN_FWD 4          /* vc_attn_fwd (needs none: 0) */
 #define VC_OP_ATTN_FWD_MX4 5      /* vc_attn_fwd_mx4 (needs none: 0) */
 #define VC_OP_VALIDATE_PERM 6     /* vc_validate_perm */
+#define VC_OP_DEMEAN_QUANT_MX6 7  /* vc_vsmooth_demean_quant_mx6 */
+#define VC_OP_ATTN_FWD_MX6 8      /* vc_attn_fwd_mx6 (needs none: 0) */
 /* vc_vsmooth_demean_quant flags */
 #define VC_DQ_NO_DEMEAN 0x1u     /* mu = 0: quantise V' itself (unsmoothed per-channel baseline) */
 #define VC_DQ_HADAMARD 0x2u      /* quantise the rotated keys K' H, scale / 128 (App. B's K pass) */
@@ -247,6 +249,34 @@ int vc_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4, c
                     float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream);
 
 /* ------------------------------------------------------------------------------------------
+ * 6-bit V-Smooth on MX formats: the 4-bit path above with E2M3 elements (OCP MX FP6) instead
+ * of E2M1, on the same matrix instructions (App. B's microscaled value quantiser, Sec. 3.2
+ * after Eq. 4; the MX element width MI355X offers between FP4 and FP8).
+ *
+ * E2M3: sign, 2-bit exponent (bias 1), 3-bit mantissa; magnitudes m/8 (m < 8), then 1 to 1.875,
+ * 2 to 3.75, 4 to 7.5 in steps of 1/8, 1/4, 1/2.  Group scale 2^E: the smallest power of two
+ * with amax <= 7.5 * 2^E (E >= -100, E = 0 for an all-zero group), stored as the byte E + 127;
+ * elements E2M3_RNE(x / 2^E).  A group of 32 elements is 32 bytes: 24 code bytes, element k in
+ * bits 6k .. 6k + 5 of the 192-bit little-endian field, then 8 zero bytes.
+ *
+ * vc_vsmooth_demean_quant_mx6: as vc_vsmooth_demean_quant_mx4, with
+ *   Kq6 [B,H,N,128]: the four 32-channel groups of each permuted row; sK6 [B,H,N,4];
+ *   Rq6 [B,H,N/128][128 channels][128]: the four 32-slot groups of each channel (slot order
+ *     as Rq4); sR6 [B,H,N/128][128][4]; mu_out bf16 [B,H,N/128,128] = bf16_RNE(mu_j).
+ *   ws: vc_demean_quant_workspace_size(B,H,N) bytes.  flags: VC_DQ_NO_DEMEAN | VC_DQ_HADAMARD.
+ *
+ * vc_attn_fwd_mx6: vc_attn_fwd_mx4's recurrence with E2M3 operands (Q per 32 channels, P per
+ *   32-key group); flags, mu and softmax_scale as vc_attn_fwd_mx4.
+ * -------------------------------------------------------------------------------------- */
+int vc_vsmooth_demean_quant_mx6(const uint16_t* K, const uint16_t* V, const int32_t* perm,
+                                int B, int H, int N, int d, unsigned flags,
+                                uint8_t* Kq6, uint8_t* sK6, uint8_t* Rq6, uint8_t* sR6,
+                                uint16_t* mu_out, void* ws, size_t ws_bytes, hipStream_t stream);
+int vc_attn_fwd_mx6(const uint16_t* Q, const uint8_t* Kq6, const uint8_t* sK6, const uint8_t* Rq6,
+                    const uint8_t* sR6, const uint16_t* mu, int B, int H, int N, int d,
+                    float softmax_scale, unsigned flags, uint16_t* O, hipStream_t stream);
+
+/* ------------------------------------------------------------------------------------------
  * Validation of a caller's permutation (Sec. 3.2, Eq. 3: pi must reorder the N keys and values
  * of each (b,h) jointly, without loss or repetition).
  *
@@ -277,6 +307,14 @@ int vc_test_e4m3_encode(const float* x, uint8_t* codes, size_t n, hipStream_t st
  * low and x[2i+1] in the high nibble (round to nearest even, |x| <= 6 expected: the callers
  * divide by the group scale first).  n (the number of floats) must be even (VC_ERR_SHAPE). */
 int vc_test_fp4_encode(const float* x, uint8_t* codes, size_t n, hipStream_t stream);
+
+/* E2M3 codes of groups of 32 float32 values as the 6-bit paths pack them: words[6i .. 6i+5]
+ * (uint32, device) hold the codes of x[32i .. 32i+31], value k in bits 6k .. 6k+5 of the
+ * 192-bit little-endian field.  With scale NULL the values are converted as they are (the
+ * quantisers divide by the group scale first, |x| <= 7.5 expected); otherwise scale[i]
+ * (float32, device, a power of two) is the conversion's own scale operand, which divides
+ * (the 6-bit attention converts P that way).  Round to nearest even. */
+int vc_test_fp6_encode(const float* x, const float* scale, uint32_t* words, size_t ngroups, hipStream_t stream);
 
 /* One k-means assignment with given centroids C [B,H,k,d] float32 (the assign step of
  * vc_vsmooth_group): labels int32 [B,H,N]; mindist float32 [B,H,N] (||v - c_z||^2 as the

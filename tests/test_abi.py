@@ -136,6 +136,48 @@ def test_mx4_argument_errors():
     assert lib.vc_test_mfma_fp8_rate(FAKE, 2 ** 31 - 1, 2 ** 31 - 1, FAKE, None) == S["VC_ERR_SHAPE"]
 
 
+def test_mx6_argument_errors():
+    lib = vc.lib()
+    f = lib.vc_vsmooth_demean_quant_mx6
+    ws = lib.vc_demean_quant_workspace_size(1, 2, 1024)
+    assert lib.vc_workspace_size(vc.VC_OP_DEMEAN_QUANT_MX6, 1, 2, 1024, 128, 0) == ws
+    assert lib.vc_workspace_size(vc.VC_OP_ATTN_FWD_MX6, 1, 2, 1024, 128, 0) == 0
+    args = lambda N=1024, d=128, flags=0, K=FAKE, nws=ws, mu=FAKE: (K, FAKE, None, 1, 2, N, d, flags, FAKE, FAKE,
+                                                                    FAKE, FAKE, mu, FAKE, nws, None)
+    assert f(*args(d=64)) == S["VC_ERR_SHAPE"]
+    assert f(*args(N=200)) == S["VC_ERR_SHAPE"]
+    assert f(*args(K=None)) == S["VC_ERR_NULL"]
+    assert f(*args(mu=None)) == S["VC_ERR_NULL"]
+    assert f(*args(flags=0x4)) == S["VC_ERR_FLAGS"]
+    assert f(*args(flags=0x3, nws=ws - 1)) == S["VC_ERR_WORKSPACE"]
+    assert f(*args(N=0)) == S["VC_OK"]
+    a = lib.vc_attn_fwd_mx6
+    P = [FAKE] * 6
+    assert a(*P, 1, 1, 128, 64, 0.0, 0, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert a(*P, 1, 1, 1 << 24, 128, 0.0, 0, FAKE, None) == S["VC_ERR_OVERFLOW"]
+    assert a(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1, 1, 128, 128, 0.0, 0, FAKE, None) == S["VC_ERR_NULL"]
+    assert a(*P, 1, 1, 128, 128, 0.0, vc.VC_ATTN_EXP_THEN_CAST, FAKE, None) == S["VC_ERR_FLAGS"]
+    assert a(*P, 1, 1, 128, 128, -1.0, vc.VC_ATTN_HADAMARD, FAKE, None) == S["VC_ERR_SHAPE"]
+    assert a(None, None, None, None, None, None, 1, 4, 0, 128, 0.0, 0, None, None) == S["VC_OK"]
+    assert lib.vc_test_fp6_encode(None, None, FAKE, 4, None) == S["VC_ERR_NULL"]
+    assert lib.vc_test_fp6_encode(FAKE, None, None, 4, None) == S["VC_ERR_NULL"]
+    assert lib.vc_test_fp6_encode(FAKE, FAKE, FAKE, 1 << 35, None) == S["VC_ERR_OVERFLOW"]
+    assert lib.vc_test_fp6_encode(None, None, None, 0, None) == S["VC_OK"]
+
+
+def test_fp6_pack_roundtrip_and_layout():
+    import numpy as np
+    rng = np.random.default_rng(5)
+    c = rng.integers(0, 64, (2, 3, 128)).astype(np.uint8)
+    p = vc.pack_fp6(c)
+    assert p.shape == c.shape and not p.reshape(-1, 32)[:, 24:].any()
+    assert np.array_equal(vc.unpack_fp6(p), c)
+    # value k in bits 6k .. 6k+5 of the group's little-endian 192-bit field
+    g = p.reshape(-1, 32)[0, :24]
+    field = int.from_bytes(bytes(g.tolist()), "little")
+    assert [(field >> (6 * k)) & 63 for k in range(32)] == c.reshape(-1, 32)[0].tolist()
+
+
 def test_fp4_pack_roundtrip():
     import torch
     c = torch.randint(0, 16, (3, 5, 128), dtype=torch.uint8)
