@@ -140,22 +140,6 @@ __device__ __forceinline__ v4i rowsum_ones4(int lane) {
   asm volatile("" : "+v"(r));
   return r;
 }
-// The same operand in E2M3, built by the conversion itself (32 ones or 32 zeros), so its bit
-// layout is the one the instruction reads.
-__device__ __forceinline__ v6i_ rowsum_ones6(int lane) {
-  const float one = rowsum_ones4_word(lane) ? 1.0f : 0.0f;
-  float x[32];
-#pragma unroll
-  for (int k = 0; k < 32; ++k) x[k] = one;
-  v6i_ r = fp6x32(x);
-  asm volatile("" : "+v"(r));
-  return r;
-}
-template <int BITS>
-__device__ __forceinline__ typename MxFmt<BITS>::frag_t rowsum_ones_mx(int lane) {
-  if constexpr (BITS == 4) return rowsum_ones4(lane);
-  else return rowsum_ones6(lane);
-}
 
 // E2M1 codes of 32 values x divided by their power-of-two group scale `scale`: nibble k = value
 // k.  The conversion instruction divides by its scale operand itself (bit for bit the codes of
@@ -185,6 +169,17 @@ __device__ __forceinline__ v6i_ pack_fp6_32(const float* x, float scale) {
   }
   return __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(lo, hi, scale);
 }
+// The row-sum operand in E2M3: 1.0 (code 0b001000) in all 32 fields of the lanes that
+// rowsum_ones4_word marks, zero elsewhere.  It is rebuilt in each matrix phase from a per-lane
+// 0/1 flag made opaque there (six selects), not kept resident: at 6 bits the 256-register
+// budget has no room for it beside the residual and key fragments.
+__device__ __forceinline__ v6i_ rowsum_ones6(uint32_t flag) {
+  asm volatile("" : "+v"(flag));
+  const int m = -(int)flag;
+  return v6i_{m & 0x08208208, m & (int)0x82082082u, m & 0x20820820, m & 0x08208208, m & (int)0x82082082u,
+              m & 0x20820820};
+}
+
 template <int BITS>
 __device__ __forceinline__ typename MxFmt<BITS>::frag_t pack_mx(const float* x, float scale) {
   if constexpr (BITS == 4) return pack_fp4_32(x, scale);
@@ -240,16 +235,24 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   const uint32_t mr0 = lds_addr(&mring[0][0]);
   constexpr int D = NBUF - 1;
   auto clampT = [&](int i) { return i < T ? i : T - 1; };
+  // the 4-byte copies' lane offset; at 6 bits made opaque at each use, so the compiler adds it
+  // to the tile address per copy instead of keeping a 64-bit per-lane address live across the
+  // loop (which the 6-bit register budget would spill)
+  auto lane4 = [&]() {
+    uint32_t o = 4 * lane;
+    if constexpr (BITS == 6) asm volatile("" : "+v"(o));
+    return o;
+  };
   auto k_tile = [&](int i, int slot) {
     dma16(Kh + (size_t)i * TILE4, so, kt0 + slot * TILE4);
     if constexpr (NC == 2) dma16(Kh + (size_t)i * TILE4, so1, kt0 + slot * TILE4 + 1024);
-    if (w < 2) dma4(sKh + (size_t)i * STILE + 256 * w, 4 * lane, ks0 + slot * STILE + 256 * w);
+    if (w < 2) dma4(sKh + (size_t)i * STILE + 256 * w, lane4(), ks0 + slot * STILE + 256 * w);
   };
   auto r_tile = [&](int i, int slot) {
     dma16(Rh + (size_t)i * TILE4, so, rt0 + slot * TILE4);
     if constexpr (NC == 2) dma16(Rh + (size_t)i * TILE4, so1, rt0 + slot * TILE4 + 1024);
-    if (w == 2 || w == 3) dma4(sRh + (size_t)i * STILE + 256 * (w - 2), 4 * lane, rs0 + slot * STILE + 256 * (w - 2));
-    if (!NO_MEAN && w == 4) dma4(muh + (size_t)i * VC_D, 4 * lane, mr0 + (i % MRING) * 256);
+    if (w == 2 || w == 3) dma4(sRh + (size_t)i * STILE + 256 * (w - 2), lane4(), rs0 + slot * STILE + 256 * (w - 2));
+    if (!NO_MEAN && w == 4) dma4(muh + (size_t)i * VC_D, lane4(), mr0 + (i % MRING) * 256);
   };
   auto issue = [&](int j) {
     k_tile(clampT(j + D), (j + D) % NBUF);
@@ -300,7 +303,12 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   }
   wait_dma_barrier<0>();
 
-  const frag_t ones = rowsum_ones_mx<BITS>(lane);
+  const v4i ones4 = rowsum_ones4(lane);   // resident at 4 bits
+  const uint32_t ones_flag = rowsum_ones4_word(lane) ? 1u : 0u;
+  auto ones = [&]() {
+    if constexpr (BITS == 4) return ones4;
+    else return rowsum_ones6(ones_flag);
+  };
   float b = 0.0f, l_run = 0.0f;   // b = -m
   // b in every element: the QK accumulator input, kept in registers and rebuilt only when b
   // changes (a running-maximum update)
@@ -382,7 +390,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
     constexpr bool QK = decltype(qk)::value, PV = decltype(pv)::value;
     frag_t kf[8];
     int ksw[4];
-    if constexpr (QK) {
+    auto load_k = [&]() {
       const uint8_t* kb_ = kt[j % NBUF];
       const uint8_t* ksb = kst[j % NBUF];
 #pragma unroll
@@ -391,15 +399,21 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
         kf[2 * kb + 1] = lds_frag<BITS>(kb_, 32 * kb + q, 2 + hl);
         ksw[kb] = (int)(*(const uint32_t*)(ksb + 4 * (32 * kb + q)) >> (8 * hl));
       }
-    }
+    };
+    // the key fragments are read first, their latency hidden behind the PV products.  (Reading
+    // them after the PV products are issued, into the residual fragments' registers, frees
+    // registers at 6 bits but gave wrong products on the device: nothing keeps the reads from
+    // overwriting a source of a product still queued on the matrix unit.)
+    if constexpr (QK) load_k();
     if constexpr (PV) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         acc[db] = mfma_mx<BITS, 0, 0>(rf[db], pw[0], acc[db], rsw[db], psc);
         acc[db] = mfma_mx<BITS, 2, 1>(rf[4 + db], pw[1], acc[db], rsw[db], psc);
       }
-      rs = mfma_mx_16<BITS, 0>(ones, pw[0], v4f{}, psc);
-      rs = mfma_mx_16<BITS, 1>(ones, pw[1], rs, psc);
+      const frag_t one = ones();
+      rs = mfma_mx_16<BITS, 0>(one, pw[0], v4f{}, psc);
+      rs = mfma_mx_16<BITS, 1>(one, pw[1], rs, psc);
     }
     if constexpr (QK) {
 #pragma unroll
