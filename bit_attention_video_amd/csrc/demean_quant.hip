@@ -554,17 +554,18 @@ __device__ __forceinline__ int pv_slot(int r) {
   return (r & 64) + 32 * ((r >> 2) & 1) + 16 * ((r >> 5) & 1) + 4 * ((r >> 3) & 3) + (r & 3);
 }
 
-// 6-bit V residual (MX E2M3), per tile j: R = V'[pi] - mu_j staged in LDS in slot order
-// [slot][channel] (float32; a thread writes four consecutive channels of one row), then
-// thread (channel, group) takes the 32 slots of its group, its maximum and scale, and writes
-// its 24 code bytes and 8 zero bytes to [channel][32 g] of the tile-transposed operand; scale
-// bytes [channel][group]; mu_out = bf16(mu_j), unscaled.
+// 6-bit V residual (MX E2M3), per tile j: the gathered rows V'[pi] staged in LDS as bf16 in
+// slot order [slot][channel] (a thread copies four channels of one row); then thread
+// (channel pair, group) takes the 32 slots of its group for both channels, R = V' - mu_j in
+// float32, each channel's maximum and scale, and writes its two 24-code-byte groups (plus 8 zero
+// bytes each) to [channel][32 g] of the tile-transposed operand; scale bytes [channel][group];
+// mu_out = bf16(mu_j), unscaled.
 __global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                  int N, const float* __restrict__ mu,
                                                  uint8_t* __restrict__ Rq6, uint8_t* __restrict__ sR6,
                                                  uint16_t* __restrict__ mu_out) {
   __shared__ float mus[VC_D];
-  __shared__ __attribute__((aligned(16))) float rs[VC_BLK * VC_D];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[VC_BLK * VC_D];
   const int bh = blockIdx.y, j = blockIdx.x, t = threadIdx.x;
   const int q4 = t & 31, rg = t >> 5;
   const int nt = N / VC_BLK;
@@ -574,37 +575,41 @@ __global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V,
     mus[t] = m;
     mu_out[tile * VC_D + t] = (uint16_t)f32_to_bf16_rne(m);
   }
-  __syncthreads();
-  const float4 m4 = *(const float4*)(mus + 4 * q4);
 #pragma unroll 4
   for (int i = 0; i < 16; ++i) {
     const int r = rg + 8 * i;
     const int tok = dq_token(perm, bh, N, j * VC_BLK + r);
-    float v[4];
-    load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
-    *(float4*)(rs + pv_slot(r) * VC_D + 4 * q4) = make_float4(v[0] - m4.x, v[1] - m4.y, v[2] - m4.z, v[3] - m4.w);
+    *(uint2*)(vs + pv_slot(r) * VC_D + 4 * q4) = *(const uint2*)(V + ((size_t)bh * N + tok) * VC_D + 4 * q4);
   }
   __syncthreads();
+  const int c2 = t & 63, g = t >> 6;
+  const float m0 = mus[2 * c2], m1 = mus[2 * c2 + 1];
+  float x0[32], x1[32];
+  float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int pidx = t + 256 * k, ch = pidx & (VC_D - 1), g = pidx >> 7;
-    float x[32];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      x[i] = rs[(32 * g + i) * VC_D + ch];
-      amax = fmaxf(amax, fabsf(x[i]));
-    }
-    const int E = mx6_exponent(amax);
-    const float inv = __builtin_ldexpf(1.0f, -E);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] *= inv;
-    const v6i w = fp6x32(x);
-    uint4* dst = (uint4*)(Rq6 + (tile * VC_D + ch) * VC_BLK + 32 * g);
-    dst[0] = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
-    dst[1] = make_uint4((uint32_t)w[4], (uint32_t)w[5], 0u, 0u);
-    sR6[(tile * VC_D + ch) * 4 + g] = (uint8_t)(E + 127);
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t w = *(const uint32_t*)(vs + (32 * g + i) * VC_D + 2 * c2);
+    x0[i] = bf16_to_f32(w & 0xFFFFu) - m0;
+    x1[i] = bf16_to_f32(w >> 16) - m1;
+    a0 = fmaxf(a0, fabsf(x0[i]));
+    a1 = fmaxf(a1, fabsf(x1[i]));
   }
+  const int E0 = mx6_exponent(a0), E1 = mx6_exponent(a1);
+  const float i0 = __builtin_ldexpf(1.0f, -E0), i1 = __builtin_ldexpf(1.0f, -E1);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    x0[i] *= i0;
+    x1[i] *= i1;
+  }
+  const v6i w0 = fp6x32(x0), w1 = fp6x32(x1);
+  uint4* d0 = (uint4*)(Rq6 + (tile * VC_D + 2 * c2) * VC_BLK + 32 * g);
+  uint4* d1 = (uint4*)(Rq6 + (tile * VC_D + 2 * c2 + 1) * VC_BLK + 32 * g);
+  d0[0] = make_uint4((uint32_t)w0[0], (uint32_t)w0[1], (uint32_t)w0[2], (uint32_t)w0[3]);
+  d0[1] = make_uint4((uint32_t)w0[4], (uint32_t)w0[5], 0u, 0u);
+  d1[0] = make_uint4((uint32_t)w1[0], (uint32_t)w1[1], (uint32_t)w1[2], (uint32_t)w1[3]);
+  d1[1] = make_uint4((uint32_t)w1[4], (uint32_t)w1[5], 0u, 0u);
+  sR6[(tile * VC_D + 2 * c2) * 4 + g] = (uint8_t)(E0 + 127);
+  sR6[(tile * VC_D + 2 * c2 + 1) * 4 + g] = (uint8_t)(E1 + 127);
 }
 
 hipError_t vc_launch_demean_quant_mx6(const uint16_t* K, const uint16_t* V, const int32_t* perm,
