@@ -503,6 +503,26 @@ def main():
     del ops4
     log(f"4-bit path: demean_quant {t_dq4:.3f} ms, attention {t_attn4:.2f} ms")
 
+    # the 6-bit path (MX E2M3 operands, P by exp2), the same way
+    ops6 = vc.vc_vsmooth_demean_quant_mx6(Kd, Vd, g["perm"])
+    e0.record()
+    for _ in range(3):
+        ops6 = vc.vc_vsmooth_demean_quant_mx6(Kd, Vd, g["perm"])
+    e1.record()
+    torch.cuda.synchronize()
+    t_dq6 = e0.elapsed_time(e1) / 3
+    attn6 = lambda: vc.vc_attn_fwd_mx6(Qd, ops6["Kq6"], ops6["sK6"], ops6["Rq6"], ops6["sR6"], ops6["mu"], out=O)
+    attn6()
+    e0.record()
+    for _ in range(3):
+        attn6()
+    e1.record()
+    torch.cuda.synchronize()
+    t_attn6 = e0.elapsed_time(e1) / 3
+    assert torch.isfinite(O.float()).all(), "non-finite attention output (6-bit)"
+    del ops6
+    log(f"6-bit path: demean_quant {t_dq6:.3f} ms, attention {t_attn6:.2f} ms")
+
     if args.attn_only_iters:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -578,6 +598,10 @@ def main():
                 "attn_tflops": round(attn_flops(B, H, N, d) / (t_attn4 * 1e-3) / 1e12, 2),
                 "attn_frac_of_fp4_peak": round(attn_flops(B, H, N, d) / (t_attn4 * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
                 "attn_over_8bit": round(t_attn4 / t_attn, 4)},
+        "mx6": {"demean_quant_ms": round(t_dq6, 4), "attn_ms": round(t_attn6, 4),
+                "attn_tflops": round(attn_flops(B, H, N, d) / (t_attn6 * 1e-3) / 1e12, 2),
+                "attn_frac_of_fp6_peak": round(attn_flops(B, H, N, d) / (t_attn6 * 1e-3) / 1e12 / FP4_PEAK_TFLOPS, 4),
+                "attn_over_8bit": round(t_attn6 / t_attn, 4)},
         "qk_rotation": {"demean_quant_ms": round(t_dq_rot, 4), "attn_ms": round(t_attn_rot, 4),
                         "attn_over_unrotated": round(t_attn_rot / t_attn, 4),
                         "demean_quant_over_unrotated": round(t_dq_rot / t_dq, 4)},
