@@ -118,14 +118,19 @@ int vc_vsmooth_group(const uint16_t* V, int B, int H, int N, int d, int k, int i
     e = vc_launch_kmeans_init(V, BH, N, k, C_out, stream);
   }
   if (e != hipSuccess) return hip_status(e);
+  // Per round: assign (which also counts the label sort's per-tile histograms), the rest of the
+  // sort, update (which also prepares the next assign's split centroids; the first round's come
+  // from the prep kernel, the last update's are not needed).
   for (int it = 0; it < iters; ++it) {
-    if ((e = vc_launch_kmeans_assign(V, C_out, BH, N, k, labels, nullptr, chi, clo, cnorm, stream)) !=
-        hipSuccess)
+    if ((e = vc_launch_kmeans_assign(V, C_out, BH, N, k, labels, nullptr, chi, clo, cnorm, it == 0, hist,
+                                     stream)) != hipSuccess)
       return hip_status(e);
-    if ((e = vc_launch_label_sort(labels, BH, N, k, hist, perm, offsets, stream)) != hipSuccess)
+    if ((e = vc_launch_label_sort(labels, BH, N, k, hist, perm, offsets, true, stream)) != hipSuccess)
       return hip_status(e);
-    double* J = it == iters - 1 ? objective : nullptr;   // J with the final labels and means
-    if ((e = vc_launch_kmeans_update(V, perm, offsets, BH, N, k, C_out, jclust, J, stream)) != hipSuccess)
+    const bool last = it == iters - 1;
+    double* J = last ? objective : nullptr;   // J with the final labels and means
+    if ((e = vc_launch_kmeans_update(V, perm, offsets, BH, N, k, C_out, jclust, J, last ? nullptr : chi, clo,
+                                     cnorm, stream)) != hipSuccess)
       return hip_status(e);
   }
   return VC_OK;
@@ -342,7 +347,8 @@ int vc_test_kmeans_assign(const uint16_t* V, const float* C, int B, int H, int N
   if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
   char* w = (char*)ws;
   return hip_status(vc_launch_kmeans_assign(V, C, B * H, N, k, labels, mindist, (uint16_t*)(w + L.chi),
-                                            (uint16_t*)(w + L.clo), (float*)(w + L.cnorm), stream));
+                                            (uint16_t*)(w + L.clo), (float*)(w + L.cnorm), true, nullptr,
+                                            stream));
 }
 
 int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_t* perm,
@@ -355,7 +361,7 @@ int vc_test_label_sort(const int32_t* labels, int B, int H, int N, int k, int32_
   vc_group_ws L = vc_group_ws_layout(B * H, N, k);
   if (ws_bytes < L.total) return VC_ERR_WORKSPACE;
   return hip_status(vc_launch_label_sort(labels, B * H, N, k, (int32_t*)((char*)ws + L.hist),
-                                         perm, offsets, stream));
+                                         perm, offsets, false, stream));
 }
 
 }  // extern "C"

@@ -7,9 +7,10 @@
 //             The products run on the bf16 matrix cores: v is exactly bf16, c is split into
 //             bf16 hi + lo parts (16 significant bits), the accumulator starts from
 //             -||c||^2 / 2 and the MFMAs add v.c in float32; each lane keeps the best of its 16
-//             centroids per block, one cross-lane exchange finishes.  A prep kernel splits the
-//             centroids and computes -||c||^2 / 2 once per (b, h) and iteration; every assign
-//             workgroup copies them into LDS.  Two centroid blocks are processed together so
+//             centroids per block, one cross-lane exchange finishes.  The split centroids and
+//             -||c||^2 / 2 are computed once per (b, h) and round (by a prep kernel for the first
+//             round, by the previous round's update afterwards); every assign workgroup copies
+//             them into LDS and also counts its 1024 labels for the label sort.  Two centroid blocks are processed together so
 //             that consecutive products belong to independent chains, and each block's best
 //             candidate comes from a depth-4 comparison tree.
 //   update    c_c = float32(sum of its rows / count), the sum in float64 in a fixed order over
@@ -67,8 +68,10 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
                                                        const uint16_t* __restrict__ plo,
                                                        const float* __restrict__ pcn, int N, int kpad,
                                                        int32_t* __restrict__ labels,
-                                                       float* __restrict__ mindist) {
+                                                       float* __restrict__ mindist,
+                                                       int32_t* __restrict__ hist) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int hcount[256];   // this tile's label histogram (the label sort's first pass)
   uint16_t* chi = (uint16_t*)smem;                     // [kpad][KM_ROW]
   uint16_t* clo = chi + (size_t)kpad * KM_ROW;         // [kpad][KM_ROW]
   float* cn = (float*)(clo + (size_t)kpad * KM_ROW);   // [kpad]
@@ -83,6 +86,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
     *(uint4*)(clo + c * KM_ROW + 8 * ch) = glo[i];
   }
   for (int c = t; c < kpad; c += KM_THREADS) cn[c] = pcn[(size_t)bh * kpad + c];
+  if (t < 256) hcount[t] = 0;
   __syncthreads();
 
   // Each wave takes 32 tokens per group (lane (q, g): token q, channel half g of every
@@ -176,7 +180,10 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
     const int oi = __shfl_xor(bi, 32, 64);
     if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
     const int tok = tok_of(grp);
-    if (tok < N && g == 0) labels[(size_t)bh * N + tok] = bi;
+    if (tok < N && g == 0) {
+      labels[(size_t)bh * N + tok] = bi;
+      if (hist) atomicAdd(&hcount[bi & 255], 1);   // integer counts: order-free
+    }
     if (mindist) {   // ||v||^2 - 2 (v.c - ||c||^2 / 2) of the winner (test output only)
       float vn = 0.0f;
 #pragma unroll
@@ -192,6 +199,10 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
 #pragma unroll
     for (int c = 0; c < 8; ++c) vcur[c] = vnext[c];
   }
+  if (hist) {   // a workgroup's 1024 tokens are one tile of the label sort
+    __syncthreads();
+    if (t < 256) hist[((size_t)bh * gridDim.x + blockIdx.x) * 256 + t] = hcount[t];
+  }
 }
 
 // Centroid update: one workgroup per (cluster, b*h); 32 row streams x 16 lanes of 8 channels.
@@ -200,14 +211,19 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
 // sums the squares of its rows and writes the cluster's objective term
 //   J_c = sum_{t in c} ||v_t||^2 - 2 c.S + n ||c||^2 = sum_{t in c} ||v_t - c||^2
 // with S the exact row sum and c the float32 centroid just stored (float64 arithmetic).
+// With chi non-null the workgroup also writes what the next assign needs of its centroid (the
+// prep kernel's bf16 hi + lo split and -||c||^2 / 2, the same operations in the same order).
 template <bool OBJ>
 __global__ __launch_bounds__(512) void k_kmeans_update(const uint16_t* __restrict__ V,
                                                        const int32_t* __restrict__ perm,
                                                        const int32_t* __restrict__ offsets,
                                                        int N, int k, float* __restrict__ C,
-                                                       double* __restrict__ jc) {
+                                                       double* __restrict__ jc, int kpad,
+                                                       uint16_t* __restrict__ chi, uint16_t* __restrict__ clo,
+                                                       float* __restrict__ cnorm) {
   __shared__ double part[32][VC_D];
   __shared__ double red[512];
+  __shared__ float crow[VC_D];
   const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int l8 = t & 15, st = t >> 4;
   const int beg = offsets[(size_t)bh * (k + 1) + c], end = offsets[(size_t)bh * (k + 1) + c + 1];
@@ -254,9 +270,24 @@ __global__ __launch_bounds__(512) void k_kmeans_update(const uint16_t* __restric
     const double n = (double)(end - beg);
     const float cf = (float)(s / n);
     C[((size_t)bh * k + c) * VC_D + t] = cf;
+    if (chi) {
+      const size_t o = ((size_t)bh * kpad + c) * VC_D + t;
+      const uint32_t hi = f32_to_bf16_rne(cf);
+      chi[o] = (uint16_t)hi;
+      clo[o] = (uint16_t)f32_to_bf16_rne(cf - bf16_to_f32(hi));
+      crow[t] = cf;
+    }
     if constexpr (OBJ) {
       const double cd = (double)cf;
       red[t] += cd * (n * cd - 2.0 * s);   // this channel's -2 c S + n c^2
+    }
+  }
+  if (chi) {
+    __syncthreads();
+    if (t == 0) {
+      float sq2 = 0.0f;
+      for (int i = 0; i < VC_D; ++i) sq2 = fmaf(crow[i], crow[i], sq2);
+      cnorm[(size_t)bh * kpad + c] = -0.5f * sq2;
     }
   }
   if constexpr (OBJ) {
@@ -302,26 +333,29 @@ static hipError_t assign_lds_limit() {
 
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
                                    int32_t* labels, float* mindist, uint16_t* chi, uint16_t* clo,
-                                   float* cn, hipStream_t s) {
+                                   float* cn, bool prep, int32_t* hist, hipStream_t s) {
   const int kpad = (k + 31) & ~31;
-  hipLaunchKernelGGL(k_kmeans_prep, dim3(kpad, BH), dim3(128), 0, s, C, k, kpad, chi, clo, cn);
+  if (prep) hipLaunchKernelGGL(k_kmeans_prep, dim3(kpad, BH), dim3(128), 0, s, C, k, kpad, chi, clo, cn);
   const size_t lds = (size_t)2 * kpad * KM_ROW * sizeof(uint16_t) + (size_t)kpad * sizeof(float);
   hipError_t e = assign_lds_limit();
   if (e != hipSuccess) return e;
   const int nblk = (N + KM_TOK_WG - 1) / KM_TOK_WG;
   hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V, (const uint16_t*)chi,
-                     (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist);
+                     (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist, hist);
   return hipGetLastError();
 }
 
 hipError_t vc_launch_kmeans_update(const uint16_t* V, const int32_t* perm, const int32_t* offsets,
-                                   int BH, int N, int k, float* C, double* jc, double* J, hipStream_t s) {
+                                   int BH, int N, int k, float* C, double* jc, double* J,
+                                   uint16_t* chi, uint16_t* clo, float* cn, hipStream_t s) {
+  const int kpad = (k + 31) & ~31;
   if (J) {
-    hipLaunchKernelGGL(k_kmeans_update<true>, dim3(k, BH), dim3(512), 0, s, V, perm, offsets, N, k, C, jc);
+    hipLaunchKernelGGL(k_kmeans_update<true>, dim3(k, BH), dim3(512), 0, s, V, perm, offsets, N, k, C, jc,
+                       kpad, chi, clo, cn);
     hipLaunchKernelGGL(k_kmeans_objective_final, dim3(BH), dim3(64), 0, s, (const double*)jc, k, J);
   } else {
     hipLaunchKernelGGL(k_kmeans_update<false>, dim3(k, BH), dim3(512), 0, s, V, perm, offsets, N, k, C,
-                       (double*)nullptr);
+                       (double*)nullptr, kpad, chi, clo, cn);
   }
   return hipGetLastError();
 }

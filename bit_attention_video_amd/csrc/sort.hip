@@ -99,9 +99,9 @@ __global__ __launch_bounds__(1024) void k_sort_scatter(const int32_t* __restrict
 }
 
 hipError_t vc_launch_label_sort(const int32_t* labels, int BH, int N, int k, int32_t* hist,
-                                int32_t* perm, int32_t* offsets, hipStream_t s) {
+                                int32_t* perm, int32_t* offsets, bool hist_ready, hipStream_t s) {
   const int nblk = (N + VC_SORT_TILE - 1) / VC_SORT_TILE;
-  hipLaunchKernelGGL(k_sort_hist, dim3(nblk, BH), dim3(256), 0, s, labels, N, nblk, hist);
+  if (!hist_ready) hipLaunchKernelGGL(k_sort_hist, dim3(nblk, BH), dim3(256), 0, s, labels, N, nblk, hist);
   hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(256), 0, s, N, nblk, k, hist, offsets);
   hipLaunchKernelGGL(k_sort_scatter, dim3(nblk, BH), dim3(1024), 0, s, labels, N, nblk,
                      (const int32_t*)hist, perm);

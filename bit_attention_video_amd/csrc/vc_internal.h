@@ -40,15 +40,21 @@ hipError_t vc_launch_test_mfma_fp8_rate(float* out, int workgroups, int iters, f
                                         hipStream_t s);
 
 hipError_t vc_launch_kmeans_init(const uint16_t* V, int BH, int N, int k, float* C, hipStream_t s);
+// Assignment with the centroids' split rows chi/clo and norms cn; with prep they are first
+// computed from C (else they are the previous update's); with hist non-null the assign
+// workgroups also write the label sort's per-tile histograms into it.
 hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, int N, int k,
                                    int32_t* labels, float* mindist, uint16_t* chi, uint16_t* clo,
-                                   float* cn, hipStream_t s);
+                                   float* cn, bool prep, int32_t* hist, hipStream_t s);
 // Update of the centroids from the sorted rows; with J non-null (the last round) also the
-// objective per (b,h) into J, via the per-cluster terms in jc.
+// objective per (b,h) into J, via the per-cluster terms in jc; with chi non-null also the split
+// rows and norms the next assign reads.
 hipError_t vc_launch_kmeans_update(const uint16_t* V, const int32_t* perm, const int32_t* offsets,
-                                   int BH, int N, int k, float* C, double* jc, double* J, hipStream_t s);
+                                   int BH, int N, int k, float* C, double* jc, double* J,
+                                   uint16_t* chi, uint16_t* clo, float* cn, hipStream_t s);
+// hist_ready: the per-tile histograms are already in hist (written by the assign kernel).
 hipError_t vc_launch_label_sort(const int32_t* labels, int BH, int N, int k, int32_t* hist,
-                                int32_t* perm, int32_t* offsets, hipStream_t s);
+                                int32_t* perm, int32_t* offsets, bool hist_ready, hipStream_t s);
 
 hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const int32_t* perm,
                                   int BH, int N, unsigned flags, uint8_t* Kq, float* sK,
