@@ -560,6 +560,8 @@ __device__ __forceinline__ int pv_slot(int r) {
 // float32, each channel's maximum and scale, and writes its two 24-code-byte groups (plus 8 zero
 // bytes each) to [channel][32 g] of the tile-transposed operand; scale bytes [channel][group];
 // mu_out = bf16(mu_j), unscaled.
+constexpr int V6_OROW = 144;   // LDS bytes per channel row of the 6-bit output tile (128 + pad)
+
 __global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V, const int32_t* __restrict__ perm,
                                                  int N, const float* __restrict__ mu,
                                                  uint8_t* __restrict__ Rq6, uint8_t* __restrict__ sR6,
@@ -575,12 +577,14 @@ __global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V,
     mus[t] = m;
     mu_out[tile * VC_D + t] = (uint16_t)f32_to_bf16_rne(m);
   }
-#pragma unroll 4
+  uint2 raw[16];   // all sixteen gathered loads in flight before any LDS write
+#pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int r = rg + 8 * i;
-    const int tok = dq_token(perm, bh, N, j * VC_BLK + r);
-    *(uint2*)(vs + pv_slot(r) * VC_D + 4 * q4) = *(const uint2*)(V + ((size_t)bh * N + tok) * VC_D + 4 * q4);
+    const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 8 * i);
+    raw[i] = *(const uint2*)(V + ((size_t)bh * N + tok) * VC_D + 4 * q4);
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) *(uint2*)(vs + pv_slot(rg + 8 * i) * VC_D + 4 * q4) = raw[i];
   __syncthreads();
   const int c2 = t & 63, g = t >> 6;
   const float m0 = mus[2 * c2], m1 = mus[2 * c2 + 1];
@@ -602,14 +606,27 @@ __global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V,
     x1[i] *= i1;
   }
   const v6i w0 = fp6x32(x0), w1 = fp6x32(x1);
-  uint4* d0 = (uint4*)(Rq6 + (tile * VC_D + 2 * c2) * VC_BLK + 32 * g);
-  uint4* d1 = (uint4*)(Rq6 + (tile * VC_D + 2 * c2 + 1) * VC_BLK + 32 * g);
+  // the codes go through LDS (rows padded to 144 bytes) so the tile leaves as one contiguous
+  // 16 KB copy rather than 32-byte pieces of 128 rows
+  __syncthreads();   // every read of vs is done
+  uint8_t* ot = (uint8_t*)vs;
+  uint4* d0 = (uint4*)(ot + (2 * c2) * V6_OROW + 32 * g);
+  uint4* d1 = (uint4*)(ot + (2 * c2 + 1) * V6_OROW + 32 * g);
   d0[0] = make_uint4((uint32_t)w0[0], (uint32_t)w0[1], (uint32_t)w0[2], (uint32_t)w0[3]);
   d0[1] = make_uint4((uint32_t)w0[4], (uint32_t)w0[5], 0u, 0u);
   d1[0] = make_uint4((uint32_t)w1[0], (uint32_t)w1[1], (uint32_t)w1[2], (uint32_t)w1[3]);
   d1[1] = make_uint4((uint32_t)w1[4], (uint32_t)w1[5], 0u, 0u);
-  sR6[(tile * VC_D + 2 * c2) * 4 + g] = (uint8_t)(E0 + 127);
-  sR6[(tile * VC_D + 2 * c2 + 1) * 4 + g] = (uint8_t)(E1 + 127);
+  uint8_t* sc = (uint8_t*)(ot + VC_D * V6_OROW);
+  sc[(2 * c2) * 4 + g] = (uint8_t)(E0 + 127);
+  sc[(2 * c2 + 1) * 4 + g] = (uint8_t)(E1 + 127);
+  __syncthreads();
+  uint8_t* dst = Rq6 + tile * VC_D * VC_BLK;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = t + 256 * i, row = c >> 3, part = c & 7;   // 16-byte chunk c of the 16 KB tile
+    *(uint4*)(dst + 16 * c) = *(const uint4*)(ot + row * V6_OROW + 16 * part);
+  }
+  if (t < VC_D) ((uint32_t*)(sR6 + tile * VC_D * 4))[t] = ((const uint32_t*)sc)[t];
 }
 
 hipError_t vc_launch_demean_quant_mx6(const uint16_t* K, const uint16_t* V, const int32_t* perm,
