@@ -361,6 +361,18 @@ __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, 
   __syncthreads();
   const float4 s4 = *(const float4*)(sc + 4 * q4);
   const float4 m4 = *(const float4*)(mus + 4 * q4);
+  // R / sV correctly rounded, as the float32 division the definition uses, from the channel's
+  // reciprocal y = RN(1 / sV) (one true division per channel instead of one per element):
+  // q1 = RN(x y) corrected once, q1 + RN(x - sV q1) y, is within one ulp of x / sV, and a second
+  // correction from an exact FMA residual then gives RN(x / sV) (Markstein's theorem: y within
+  // half an ulp of 1 / sV, q1 within one ulp of x / sV, no underflow or overflow; the quotients
+  // here lie in [-448, 448] and the residuals are far from the subnormal range).
+  const float4 y4 = make_float4(1.0f / s4.x, 1.0f / s4.y, 1.0f / s4.z, 1.0f / s4.w);
+  auto qdiv = [](float x, float sv, float y) {
+    float q = x * y;
+    q = fmaf(fmaf(-q, sv, x), y, q);
+    return fmaf(fmaf(-q, sv, x), y, q);
+  };
   // Thread (q4, rg) takes the 4-row groups rg, rg+8, rg+16, rg+24 of the tile and channels
   // 4 q4 .. 4 q4 + 3.  The rows 4 G .. 4 G + 3 of a group land in 4 consecutive PV slots, so
   // each channel's four codes form one 32-bit word of the transposed tile.
@@ -373,8 +385,8 @@ __global__ __launch_bounds__(256) void k_vpass2(const uint16_t* __restrict__ V, 
       const int tok = dq_token(perm, bh, N, j * VC_BLK + r0 + i4);
       float v[4];
       load4(V + ((size_t)bh * N + tok) * VC_D + 4 * q4, v);
-      const uint32_t w = e4m3x4((v[0] - m4.x) / s4.x, (v[1] - m4.y) / s4.y,
-                                (v[2] - m4.z) / s4.z, (v[3] - m4.w) / s4.w);
+      const uint32_t w = e4m3x4(qdiv(v[0] - m4.x, s4.x, y4.x), qdiv(v[1] - m4.y, s4.y, y4.y),
+                                qdiv(v[2] - m4.z, s4.z, y4.z), qdiv(v[3] - m4.w, s4.w, y4.w));
 #pragma unroll
       for (int e = 0; e < 4; ++e) wc[e] |= ((w >> (8 * e)) & 0xFFu) << (8 * i4);
     }
