@@ -554,6 +554,14 @@ def main():
     fp8_peak_meas, clock_ghz = measured_fp8_peak(vc, torch)
     log(f"measured dense FP8 rate {fp8_peak_meas:.0f} TFLOP/s at a {clock_ghz:.2f} GHz shader clock "
         f"(vendor figure {FP8_PEAK_TFLOPS:.0f})")
+    # the HBM bandwidth a plain device-to-device copy reaches on this part (read + write bytes),
+    # the practical ceiling beside which the V-Smooth kernels' GB/s read
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = time_ms(torch, lambda: dst.copy_(src), 10)
+    copy_gbs = 2.0 * (1 << 30) / (t_copy * 1e-3) / 1e9
+    del src, dst
+    log(f"plain device copy of 1 GiB: {t_copy:.3f} ms = {copy_gbs:.0f} GB/s (read + write)")
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
         with open(PROFILE_TRAFFIC) as f:
@@ -591,6 +599,7 @@ def main():
         "attn_ms": round(t_attn, 4), "attn_tflops": round(attn_tflops, 2),
         "group_ms": round(t_group, 4), "demean_quant_ms": round(t_dq, 4),
         "demean_quant_gbs": round(dq_bytes / (t_dq * 1e-3) / 1e9, 1),
+        "hbm_copy_gbs": round(copy_gbs, 1),
         "vsmooth_over_attn": {k2: round(v2, 4) for k2, v2 in amort.items()},
         "p_path": {"expcast_ms": round(t_attn, 4), "exp_then_cast_ms": round(t_etc, 4),
                    "expcast_speedup": round(t_etc / t_attn, 4)},
