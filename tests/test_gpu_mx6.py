@@ -187,3 +187,41 @@ def test_mx6_empty_is_noop():
                              torch.empty((1, 2, 0, 128, 4), dtype=torch.uint8, device=DEV),
                              torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=DEV))
     assert out.shape == (1, 2, 0, 128)
+
+
+@pytest.mark.parametrize("fmt_bits", [4, 6])
+@pytest.mark.parametrize("mag", [1e-4, 1e4])
+def test_mx_paths_extreme_magnitudes(fmt_bits, mag):
+    """Inputs scaled by 1e-4 and 1e4 through the 4-bit and the 6-bit path: the per-32 scales
+    follow, the quantised operands stay bit-exact and the output matches the emulated oracle."""
+    fmt = "e2m1" if fmt_bits == 4 else "e2m3"
+    rng = np.random.default_rng(15)
+    N = 512
+    Q = F.bf16_bits_from_value(F.bf16_round(rng.standard_normal((1, 1, N, 128)) * mag))
+    K = F.bf16_bits_from_value(F.bf16_round((rng.standard_normal((1, 1, N, 128)) + 1.0) * mag))
+    V = F.bf16_bits_from_value(F.bf16_round((rng.standard_normal((1, 1, N, 128)) + 2.0) * mag))
+    perm = rng.permutation(N).astype(np.int32)
+    Qh, Kh, Vh = values(Q[0, 0]), values(K[0, 0]), values(V[0, 0])
+    scale = 1.0 / (mag * mag * np.sqrt(128.0))   # keeps the scores O(1)
+    pd = torch.from_numpy(perm[None, None]).to(DEV)
+    if fmt_bits == 4:
+        dev = vc.vc_vsmooth_demean_quant_mx4(bf16_dev(K), bf16_dev(V), pd)
+        kc_g = vc.unpack_fp4(dev["Kq4"]).cpu().numpy()[0, 0]
+        O = vc.vc_attn_fwd_mx4(bf16_dev(Q), dev["Kq4"], dev["sK4"], dev["Rq4"], dev["sR4"], dev["mu"],
+                               softmax_scale=float(scale))
+        sk_g = dev["sK4"].cpu().numpy()[0, 0].astype(np.int64) - 127
+    else:
+        dev = vc.vc_vsmooth_demean_quant_mx6(bf16_dev(K), bf16_dev(V), pd)
+        kc_g = vc.unpack_fp6(dev["Kq6"].cpu().numpy()[0, 0])
+        O = vc.vc_attn_fwd_mx6(bf16_dev(Q), dev["Kq6"], dev["sK6"], dev["Rq6"], dev["sR6"], dev["mu"],
+                               softmax_scale=float(scale))
+        sk_g = dev["sK6"].cpu().numpy()[0, 0].astype(np.int64) - 127
+    qc, qE = M.quantize_q4(Qh, scale, fmt=fmt)
+    kc, kE = M.quantize_k4(Kh, perm, fmt=fmt)
+    vq = M.quantize_v4(Vh, perm, fmt=fmt)
+    assert np.array_equal(kc_g, kc) and np.array_equal(sk_g, kE)
+    ref = M.attention_tiled_mx4(M.dequant_row_groups(qc, qE, fmt), M.dequant_row_groups(kc, kE, fmt),
+                                M.dequant_v4(vq["codes"], vq["E"], fmt), vq["mu_b"], fmt=fmt)
+    err = T.rel_l2(values(bf16_host_bits(O))[0, 0], ref)
+    note(f"  {fmt_bits}-bit, magnitude {mag}: rel-L2 vs emulated {err:.3e}")
+    assert err < TOL
