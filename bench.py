@@ -112,11 +112,12 @@ def attn_clock_probe(vc, torch, Qd, ops, O, reps=5):
     return e0.elapsed_time(e1) / reps, float(ghz)
 
 
-def accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads, nrows=256):
+def accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads, nrows=256, O4=None, O6=None):
     """Accuracy of the timed path on sampled heads (computed after the timed region): the GPU output
     against the oracle's emulated recurrence on the GPU's permutation and against FP64 exact
     attention; the two unsmoothed sequence-order baselines (same P path, and exp-then-cast P)
-    against exact; the grouping objective against the oracle's Lloyd from the same start."""
+    against exact; the grouping objective against the oracle's Lloyd from the same start; and,
+    when given, the 4-bit and 6-bit paths' outputs on the same permutation against exact."""
     from oracle import attention as T
     from oracle import formats as F
     from oracle import vsmooth as S
@@ -125,8 +126,10 @@ def accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads, nrows=256):
     J = g["J"].cpu().numpy()
     val = lambda t: F.bf16_value_from_bits(t.cpu().view(torch.int16).numpy().view(np.uint16))
     O, Ob, Oe = val(O), val(Ob), val(Oe)
+    O4 = val(O4) if O4 is not None else None
+    O6 = val(O6) if O6 is not None else None
     rows = np.unique(np.linspace(0, cfg.N - 1, nrows).round().astype(np.int64))
-    r = {"emu": [], "vc": [], "base": [], "etc": [], "J": []}
+    r = {"emu": [], "vc": [], "base": [], "etc": [], "J": [], "mx4": [], "mx6": []}
     for h in heads:
         Qh, Kh, Vh = (F.bf16_value_from_bits(x[0, h]) for x in (Q, K, V))
         qc, sQ = S.quantize_q(Qh)
@@ -139,6 +142,10 @@ def accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads, nrows=256):
         r["vc"].append(T.rel_l2(O[0, h][rows], exact))
         r["base"].append(T.rel_l2(Ob[0, h][rows], exact))
         r["etc"].append(T.rel_l2(Oe[0, h][rows], exact))
+        if O4 is not None:
+            r["mx4"].append(T.rel_l2(O4[0, h][rows], exact))
+        if O6 is not None:
+            r["mx6"].append(T.rel_l2(O6[0, h][rows], exact))
         J_ref = S.vsmooth_group(Vh, cfg.k, cfg.iters)["J"]
         r["J"].append(abs(float(J[0, h]) - J_ref) / J_ref)
     mean = lambda k: float(np.mean(r[k]))
@@ -148,7 +155,9 @@ def accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads, nrows=256):
             "unsmoothed_same_p_vs_exact": round(mean("base"), 6),
             "unsmoothed_exp_then_cast_vs_exact": round(mean("etc"), 6),
             "vc_below_unsmoothed": mean("vc") < mean("base"),
-            "kmeans_J_rel_err_max": float(f"{max(r['J']):.3e}")}
+            "kmeans_J_rel_err_max": float(f"{max(r['J']):.3e}"),
+            **({"mx4_vs_exact": round(mean("mx4"), 6)} if r["mx4"] else {}),
+            **({"mx6_vs_exact": round(mean("mx6"), 6)} if r["mx6"] else {})}
 
 
 def time_ms(torch, fn, reps):
@@ -628,8 +637,10 @@ def main():
         Ob = vc.vc_attn_fwd(*bargs, no_mean=True)
         Oe = vc.vc_attn_fwd(*bargs, no_mean=True, exp_then_cast=True)
         O = vc.vc_attn_fwd(Qd, ops["Kq"], ops["sK"], ops["Rq"], ops["mu"], ops["sV"])
-        out["accuracy"] = accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads=sorted({0, H // 2, H - 1}))
-        del base, Ob, Oe
+        O4 = vc.vc_attention_mx4(Qd, Kd, Vd, g["perm"])
+        O6 = vc.vc_attention_mx6(Qd, Kd, Vd, g["perm"])
+        out["accuracy"] = accuracy(cfg, Q, K, V, g, O, Ob, Oe, heads=sorted({0, H // 2, H - 1}), O4=O4, O6=O6)
+        del base, Ob, Oe, O4, O6
         log(f"accuracy: {json.dumps(out['accuracy'])}")
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
