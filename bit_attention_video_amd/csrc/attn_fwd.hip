@@ -134,7 +134,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   __shared__ __attribute__((aligned(1024))) uint8_t tiles[NBUF][2][TILE_BYTES];
   __shared__ __attribute__((aligned(256))) uint16_t mring[MRING][128];
   // first-half row sums of each query row, and b at the time they were saved
-  __shared__ __attribute__((aligned(16))) float rsnap[NWAVE * 32][12];
+  __shared__ float rsnap[9][NWAVE * 32];   // [slot][query of the workgroup]
   __shared__ float red[NWAVE];
 
   const int t = threadIdx.x, lane = t & 63, q = lane & 31, hl = lane >> 5;
@@ -229,14 +229,16 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   // b in every element: the QK accumulator input, kept in registers and rebuilt only when b
   // changes (a running-maximum update), not once per tile
   v16f bsplat = {};
-  // E8M0 exponent of sK of the tile of this wave's next QK product.  It is read in the vector
-  // phase before: a scalar load shares its wait counter with the LDS reads, and waiting for it
-  // inside the matrix phase would also wait for every fragment in flight.
+  // E8M0 exponent of sK of the tile of this wave's next QK product.  It is loaded at the start
+  // of the vector phase before and taken before that phase's LDS reads: a scalar load shares its
+  // wait counter with the LDS reads, so waiting for it later (or inside the matrix phase) would
+  // also wait for every fragment in flight.
   auto e8m0_sk = [&](int i) { return (int)((__float_as_uint(sKh[i]) >> 23) & 0xFFu); };
   int sa = e8m0_sk(0);
   // Row sums of the current 16-tile group (query q), kept as a shift register: each tile's r
   // enters rA[7] and pushes the older ones down.  After the group's 8th tile rA is saved to
-  // LDS (rsnap, with the b of that moment) and restarts; the saved half is rescaled once, at
+  // LDS (rsnap, one dword per slot and query, so the stores need no register quad; with the b
+  // of that moment) and restarts; the saved half is rescaled once, at
   // the group end, by 2^((b_end - b_snap)/8), the product of the maximum updates since.  At
   // the group end the saved half holds tiles t0 .. t0+7 and rA[k] tile e-7+k (zero for tiles
   // before t0+8): the bf16 instruction's K-slots of the lane halves 0 and 1.
@@ -244,17 +246,17 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
 #pragma unroll
   for (int k = 0; k < 8; ++k) rA[k] = 0.0f;
   bool snapped = false;   // a first half of the current group is in rsnap
-  float* my_snap = &rsnap[w * 32 + q][0];
+  float* my_snap = &rsnap[0][w * 32 + q];   // slot i at my_snap[i * NWAVE * 32]
   auto push_r = [&](float r, int e) {   // r of tile e
 #pragma unroll
     for (int k = 0; k < 7; ++k) rA[k] = rA[k + 1];
     rA[7] = r;
     if ((e & 15) == 7) {
-      *(float4*)my_snap = make_float4(rA[0], rA[1], rA[2], rA[3]);
-      *(float4*)(my_snap + 4) = make_float4(rA[4], rA[5], rA[6], rA[7]);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) my_snap[k * NWAVE * 32] = rA[k];
 #pragma unroll
       for (int k = 0; k < 8; ++k) rA[k] = 0.0f;
-      my_snap[8] = b;
+      my_snap[8 * NWAVE * 32] = b;
       snapped = true;
     }
   };
@@ -274,10 +276,9 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   auto mean_group = [&](int e) {
     float rB[8];
     if (snapped) {
-      const float4 s0 = *(const float4*)my_snap, s1 = *(const float4*)(my_snap + 4);
-      const float f = __builtin_amdgcn_exp2f(0.125f * (b - my_snap[8]));
-      rB[0] = s0.x * f; rB[1] = s0.y * f; rB[2] = s0.z * f; rB[3] = s0.w * f;
-      rB[4] = s1.x * f; rB[5] = s1.y * f; rB[6] = s1.z * f; rB[7] = s1.w * f;
+      const float f = __builtin_amdgcn_exp2f(0.125f * (b - my_snap[8 * NWAVE * 32]));
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rB[k] = my_snap[k * NWAVE * 32] * f;
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) rB[k] = 0.0f;
@@ -308,7 +309,9 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     }
   };
 
-  // M(j): A += P R and the row sum of tile j-1, then S^T of tile j (t = a s + b).  All
+  // M(j): A += P R and the row sum of tile j-1, then S^T of tile j (t = a s + b), then r of
+  // tile j-1 into l and rho (vector work that fills the wave's idle issue slots while its
+  // products run, taken off the vector phase).  All
   // fragments of the residual tile are requested first and two key fragments after each PV
   // instruction, so the matrix unit never waits for an LDS round trip inside the phase.
   auto mphase = [&](int j, auto qk, auto pv) {
@@ -359,21 +362,20 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-    // the group that ended at tile j-2 has all its row sums in rho since V(j-1)
-    if constexpr (PV)
+    // the group that ended at tile j-2 has all its row sums in rho since M(j-1)
+    if constexpr (PV) {
       if (!NO_MEAN && j >= 2 && ((j - 2) & 15) == 15) mean_group(j - 2);
+      const float r = rs[0];   // r of tile j-1 into l and rho
+      l_run += r;
+      if (!NO_MEAN) push_r(r, j - 1);
+    }
   };
   constexpr std::true_type Y{};
   constexpr std::false_type X{};
 
-  // V(j): r of tile j-1 into l and rho, running maximum of tile j, its ExpCast codes
-  // (on the first tile rs is still zero, so the r insertion is a no-op)
+  // V(j): running maximum of tile j, its ExpCast codes, the residual fragments of PV(j)
   auto vphase = [&](int j) {
-    {
-      const float r = rs[0];
-      l_run += r;
-      if (!NO_MEAN) push_r(r, j - 1);
-    }
+    const int sa_next = e8m0_sk(j + 1 < T ? j + 1 : T - 1);   // for QK of tile j+1
     float tm;
     if constexpr (ETC) {
       tm = -__builtin_inff();
@@ -422,6 +424,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
     // key half 0's codes free the scores of key blocks 0-1, which then receive the residual
     // fragments of PV half 0 while key half 1 is converted
+    sa = sa_next;   // its wait precedes the fragment reads
+    keep(sa);
     const uint8_t* rb = tiles[j % NBUF][1];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
@@ -449,8 +453,6 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
 #pragma unroll
       for (int db = 0; db < 4; ++db) rf[4 * p + db] = frag(rb, p ? co2 : co0, p ? co3 : co1, db);
     }
-    sa = e8m0_sk(j + 1 < T ? j + 1 : T - 1);   // for QK of tile j+1
-    keep(sa);
   };
 
   // Phases 2j and 2j+1.  Group 0 runs M(j) | V(j), group 1 V(j-1) | M(j); each wave issues
@@ -503,15 +505,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     wait_dma_barrier<0>();
   }
 
-  // ---- epilogue: r of the last tile, the last mean group, O = A * sV / l -> bf16 ----
-  {
-    const float r = rs[0];
-    l_run += r;
-    if (!NO_MEAN) {
-      push_r(r, T - 1);
-      mean_group(T - 1);
-    }
-  }
+  // ---- epilogue: the last mean group, O = A * sV / l -> bf16 ----
+  if (!NO_MEAN) mean_group(T - 1);
   const float inv_l = 1.0f / l_run;
   const float* sv = sV + (size_t)bh * VC_D;
   uint16_t* orow = O + (headN + qi) * VC_D;

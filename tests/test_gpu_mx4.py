@@ -17,6 +17,12 @@ from gpu_util import DEV, bf16_dev, bf16_host_bits, config_inputs, note, rows_sa
 pytestmark = pytest.mark.gpu
 
 TOL = 5e-3
+# Without the rotation the kernel takes the oracle's steps one for one on the same operands, so
+# it differs from the emulated recurrence only where a float32 summation order flips a P code:
+# 1e-9 to 7e-5 measured.  A corrupted operand (a fragment register overwritten while its product
+# still waits on the matrix unit) moved whole query blocks by 1e-3 to 3e-3, inside TOL, so the
+# on-operand parity also holds this bound.
+TIGHT = 5e-4
 
 
 def test_fp4_conversion_matches_oracle():
@@ -106,7 +112,7 @@ def test_mx4_attention_on_oracle_operands(name, heads, nrows, had):
     for h in range(H):
         err = T.rel_l2(O[0, h][rows], _emulated(ops[h], rows))
         note(f"  head {h}: rel-L2 vs emulated = {err:.3e}")
-        assert err < TOL
+        assert err < (TOL if had else TIGHT)
 
 
 def test_mx4_no_mean_flag():
