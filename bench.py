@@ -33,12 +33,17 @@ ATTN_SOURCES = ["bit_attention_video_amd/csrc/attn_fwd.hip", "bit_attention_vide
 
 
 def attn_source_hash():
-    """Hash of the attention kernel's sources: counters taken on other sources are stale."""
+    """Hash of the attention kernel's sources, comments and blank lines left out: counters
+    taken on other code are stale, while a comment edit does not change the kernel."""
     import hashlib
+    import re
+    tok = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            code = tok.sub(lambda m: "" if m.group(0).startswith("/") else m.group(0), fh.read())
+        lines = [ln.rstrip() for ln in code.split("\n")]
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 

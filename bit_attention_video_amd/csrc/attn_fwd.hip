@@ -7,10 +7,11 @@
 // LDS, filled by direct global->LDS copies that every wave shares.
 //
 // Ping-pong between the two groups.  Per tile a wave has a matrix part M(j) -- the PV
-// product and the row sum of tile j-1, then the QK product of tile j -- and a vector part
-// V(j): the running maximum and the ExpCast codes of tile j, each key half of codes followed
-// by the read of the next PV product's residual fragments for that half into the registers
-// its scores just freed.  The groups run them in
+// product and the row sum of tile j-1, then the QK product of tile j, then the bookkeeping of
+// that row sum (l and the mean term's shift register) while the products run -- and a vector
+// part V(j): the running maximum and the ExpCast codes of tile j, each key half of codes
+// followed by the read of the next PV product's residual fragments for that half into the
+// registers its scores just freed.  The groups run them in
 // opposite phases separated by workgroup barriers (group 0: M(j) | V(j), group 1:
 // V(j-1) | M(j)).  A SIMD holds one wave of each group, so while one of them keeps the
 // matrix unit busy the other does the vector work; with one workgroup per CU nothing else
