@@ -423,8 +423,8 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     }
     // ExpCast Round + clip: one saturating RNE byte conversion per element.  Byte jj of the
     // PV B-operand for key half p is element (kb = 2p + jj/16, i = jj%16) of S^T.
-    // key half 0's codes free the scores of key blocks 0-1, which then receive the residual
-    // fragments of PV half 0 while key half 1 is converted
+    // key half 0's codes free the scores of key blocks 0-1, whose registers then receive the
+    // residual fragments of PV half 0 (the reads are requested in key-half order)
     sa = sa_next;   // its wait precedes the fragment reads
     keep(sa);
     const uint8_t* rb = tiles[j % NBUF][1];
