@@ -31,7 +31,7 @@ def test_source_key_ignores_comments_not_code(tmp_path, monkeypatch):
     main.write_text(text + '\nstatic const char* k = "// not a comment";\n')
     assert bench.attn_source_hash() != key
     # any code change changes the key
-    main.write_text(text.replace("NBUF", "NBUF ", 1) if "NBUF" in text else text + "\nint x;\n")
+    main.write_text(text + "\nstatic int unused_probe;\n")
     assert bench.attn_source_hash() != key
 
 
