@@ -35,7 +35,8 @@ int vc_hip_status(hipError_t e) { return hip_status(e); }
 
 vc_group_ws vc_group_ws_layout(int BH, int N, int k) {
   vc_group_ws L;
-  size_t nblk = (size_t)(N + VC_SORT_TILE - 1) / VC_SORT_TILE;
+  const int tile = vc_group_tile(BH, N);
+  size_t nblk = (size_t)(N + tile - 1) / tile;
   size_t kpad = (size_t)((k + 31) & ~31);
   size_t off = 0;
   L.hist = off;  off = align256(off + (size_t)BH * nblk * 256 * sizeof(int32_t));
@@ -49,7 +50,8 @@ vc_group_ws vc_group_ws_layout(int BH, int N, int k) {
 
 vc_dq_ws vc_dq_ws_layout(int BH, int N) {
   vc_dq_ws L;
-  size_t nchunk = (size_t)(N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  const int chunk = vc_kstat_chunk(BH, N);
+  size_t nchunk = (size_t)(N + chunk - 1) / chunk;
   size_t off = 0;
   L.kpart = off; off = align256(off + (size_t)BH * nchunk * 128 * sizeof(double));
   L.kbar = off;  off = align256(off + (size_t)BH * 128 * sizeof(float));

@@ -8,7 +8,7 @@
 //
 // Passes (all grids are (blocks, b*h); 256 or 512 threads = 32 channel quads x 8 or 16 row
 // groups):
-//   k_kstat_partial  float64 channel sums of K per 1024-row chunk
+//   k_kstat_partial  float64 channel sums of K per 1024-row chunk (256 for small shapes)
 //   k_kstat_final    kbar = float32(sum / N) in chunk order
 //   k_kquant         per 128-row block of K[pi]: K' = K - kbar, sK = 2^E (smallest power of two
 //                    with amax <= 448 sK, an E8M0 block scale), codes
@@ -51,15 +51,15 @@ __device__ __forceinline__ float block_max_512(float v, float* red8) {
 }
 
 __global__ __launch_bounds__(256) void k_kstat_partial(const uint16_t* __restrict__ K, int N, int nchunk,
-                                                       double* __restrict__ kpart) {
+                                                       int chunk, double* __restrict__ kpart) {
   __shared__ double part[8][VC_D];
   const int bh = blockIdx.y, ch = blockIdx.x, t = threadIdx.x;
   const int q4 = t & 31, rg = t >> 5;
   double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-  const int r0 = ch * VC_KSTAT_CHUNK;
+  const int r0 = ch * chunk;
   // 64 rows per step, 8 loads in flight per thread; N is a multiple of 64, so a step that
   // starts inside the matrix ends inside it.
-  for (int g = 0; g < VC_KSTAT_CHUNK / 64; ++g) {
+  for (int g = 0; g < chunk / 64; ++g) {
     const int rb = r0 + 64 * g + rg;
     if (rb >= N) break;
     float v[8][4];
@@ -645,13 +645,14 @@ hipError_t vc_launch_demean_quant_mx6(const uint16_t* K, const uint16_t* V, cons
                                       int BH, int N, unsigned flags, uint8_t* Kq6, uint8_t* sK6,
                                       uint8_t* Rq6, uint8_t* sR6, uint16_t* mu_out, char* ws,
                                       const vc_dq_ws& L, hipStream_t s) {
-  const int nchunk = (N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  const int chunk = vc_kstat_chunk(BH, N);
+  const int nchunk = (N + chunk - 1) / chunk;
   const int nt = N / VC_BLK;
   double* kpart = (double*)(ws + L.kpart);
   float* kbar = (float*)(ws + L.kbar);
   float* mu = (float*)(ws + L.mu);
   float* amaxp = (float*)(ws + L.amaxp);
-  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
+  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, chunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
   if (flags & VC_DQ_HADAMARD)
     hipLaunchKernelGGL(k_kquant6<true>, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq6, sK6);
@@ -667,13 +668,14 @@ hipError_t vc_launch_demean_quant_mx4(const uint16_t* K, const uint16_t* V, cons
                                       int BH, int N, unsigned flags, uint8_t* Kq4, uint8_t* sK4,
                                       uint8_t* Rq4, uint8_t* sR4, uint16_t* mu_out, char* ws,
                                       const vc_dq_ws& L, hipStream_t s) {
-  const int nchunk = (N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  const int chunk = vc_kstat_chunk(BH, N);
+  const int nchunk = (N + chunk - 1) / chunk;
   const int nt = N / VC_BLK;
   double* kpart = (double*)(ws + L.kpart);
   float* kbar = (float*)(ws + L.kbar);
   float* mu = (float*)(ws + L.mu);
   float* amaxp = (float*)(ws + L.amaxp);
-  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
+  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, chunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
   if (flags & VC_DQ_HADAMARD)
     hipLaunchKernelGGL(k_kquant4<true>, dim3(nt, BH), dim3(256), 0, s, K, perm, (const float*)kbar, N, Kq4, sK4);
@@ -690,13 +692,14 @@ hipError_t vc_launch_demean_quant(const uint16_t* K, const uint16_t* V, const in
                                   int BH, int N, unsigned flags, uint8_t* Kq, float* sK,
                                   uint8_t* Rq, uint16_t* mu_out, float* sV, char* ws,
                                   const vc_dq_ws& L, hipStream_t s) {
-  const int nchunk = (N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK;
+  const int chunk = vc_kstat_chunk(BH, N);
+  const int nchunk = (N + chunk - 1) / chunk;
   const int nt = N / VC_BLK;
   double* kpart = (double*)(ws + L.kpart);
   float* kbar = (float*)(ws + L.kbar);
   float* mu = (float*)(ws + L.mu);
   float* amaxp = (float*)(ws + L.amaxp);
-  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, kpart);
+  hipLaunchKernelGGL(k_kstat_partial, dim3(nchunk, BH), dim3(256), 0, s, K, N, nchunk, chunk, kpart);
   hipLaunchKernelGGL(k_kstat_final, dim3(BH), dim3(128), 0, s, (const double*)kpart, N, nchunk, kbar);
   if (flags & VC_DQ_HADAMARD)
     hipLaunchKernelGGL(k_kquant_had, dim3(nt, BH), dim3(512), 0, s, K, perm, (const float*)kbar, N, Kq, sK);

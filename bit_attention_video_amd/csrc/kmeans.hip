@@ -10,9 +10,10 @@
 //             centroids per block, one cross-lane exchange finishes.  The split centroids and
 //             -||c||^2 / 2 are computed once per (b, h) and round (by a prep kernel for the first
 //             round, by the previous round's update afterwards); every assign workgroup copies
-//             them into LDS and also counts its 1024 labels for the label sort.  Two centroid blocks are processed together so
-//             that consecutive products belong to independent chains, and each block's best
-//             candidate comes from a depth-4 comparison tree.
+//             them into LDS and also counts its labels for the label sort (a workgroup's tokens,
+//             1024 or for small shapes 256, are one sort tile).  Two centroid blocks are
+//             processed together so that consecutive products belong to independent chains, and
+//             each block's best candidate comes from a depth-4 comparison tree.
 //   update    c_c = float32(sum of its rows / count), the sum in float64 in a fixed order over
 //             the rows of cluster c in sorted order (perm, offsets from the label sort); an
 //             empty cluster keeps its centroid.
@@ -26,7 +27,6 @@
 
 #include <atomic>
 
-constexpr int KM_TOK_WG = 1024;  // tokens per assign workgroup (8 waves x 4 groups x 32)
 constexpr int KM_THREADS = 512;  // assign workgroup size
 constexpr int KM_ROW = 136;      // LDS row stride in bf16: 128 + 8 pad = 272 bytes
 
@@ -63,6 +63,8 @@ __global__ __launch_bounds__(128) void k_kmeans_prep(const float* __restrict__ C
   }
 }
 
+// TOK tokens per workgroup (8 waves x TOK/256 groups x 32): one label-sort tile.
+template <int TOK>
 __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restrict__ V,
                                                        const uint16_t* __restrict__ phi,
                                                        const uint16_t* __restrict__ plo,
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
   const int w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
   const int nblk = kpad >> 5;
   const uint16_t* Vb = V + (size_t)bh * N * VC_D + 8 * g;
-  auto tok_of = [&](int grp) { return blockIdx.x * KM_TOK_WG + grp * (KM_THREADS / 2) + w * 32 + q; };
+  auto tok_of = [&](int grp) { return blockIdx.x * TOK + grp * (KM_THREADS / 2) + w * 32 + q; };
   auto load_rows = [&](int grp, v8s (&vb)[8]) {
     const int tok = tok_of(grp);
     const uint16_t* vrow = Vb + (size_t)(tok < N ? tok : N - 1) * VC_D;
@@ -105,8 +107,8 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
   v8s vcur[8], vnext[8];
   load_rows(0, vcur);
 #pragma unroll
-  for (int grp = 0; grp < KM_TOK_WG / (KM_THREADS / 2); ++grp) {
-    if (grp + 1 < KM_TOK_WG / (KM_THREADS / 2)) load_rows(grp + 1, vnext);
+  for (int grp = 0; grp < TOK / (KM_THREADS / 2); ++grp) {
+    if (grp + 1 < TOK / (KM_THREADS / 2)) load_rows(grp + 1, vnext);
     float best = -__builtin_inff();   // max of v.c - ||c||^2 / 2
     int bi = 0;
     // Block cb's accumulator starts from -||c||^2 / 2 of this lane's 16 candidates,
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
 #pragma unroll
     for (int c = 0; c < 8; ++c) vcur[c] = vnext[c];
   }
-  if (hist) {   // a workgroup's 1024 tokens are one tile of the label sort
+  if (hist) {   // a workgroup's TOK tokens are one tile of the label sort
     __syncthreads();
     if (t < 256) hist[((size_t)bh * gridDim.x + blockIdx.x) * 256 + t] = hcount[t];
   }
@@ -326,7 +328,11 @@ static hipError_t assign_lds_limit() {
   const unsigned long long bit = dev < 64 ? (1ull << dev) : 0ull;
   if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
   const size_t lds_max = (size_t)2 * VC_MAX_K * KM_ROW * sizeof(uint16_t) + (size_t)VC_MAX_K * sizeof(float);
-  e = hipFuncSetAttribute((const void*)k_kmeans_assign, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
+  e = hipFuncSetAttribute((const void*)k_kmeans_assign<VC_SORT_TILE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)lds_max);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute((const void*)k_kmeans_assign<VC_SORT_TILE_SMALL>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
   if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
   return e;
 }
@@ -339,9 +345,14 @@ hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, in
   const size_t lds = (size_t)2 * kpad * KM_ROW * sizeof(uint16_t) + (size_t)kpad * sizeof(float);
   hipError_t e = assign_lds_limit();
   if (e != hipSuccess) return e;
-  const int nblk = (N + KM_TOK_WG - 1) / KM_TOK_WG;
-  hipLaunchKernelGGL(k_kmeans_assign, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V, (const uint16_t*)chi,
-                     (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist, hist);
+  const int tile = vc_group_tile(BH, N);   // the label sort's tile, whose histograms hist holds
+  const int nblk = (N + tile - 1) / tile;
+  if (tile == VC_SORT_TILE)
+    hipLaunchKernelGGL(k_kmeans_assign<VC_SORT_TILE>, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V,
+                       (const uint16_t*)chi, (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist, hist);
+  else
+    hipLaunchKernelGGL(k_kmeans_assign<VC_SORT_TILE_SMALL>, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V,
+                       (const uint16_t*)chi, (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist, hist);
   return hipGetLastError();
 }
 

@@ -1,16 +1,18 @@
 // Stable counting sort of cluster labels (VC-Attention Sec. 3.2, Eq. 3: pi = argsort(z)).
 //
 // k <= 256, so one 8-bit digit suffices.  Three deterministic passes per (b, h):
-//   1. per 1024-token tile, a label histogram (integer LDS atomics: order-free);
+//   1. per tile of 1024 (or, for small shapes, 256) tokens, a label histogram (integer LDS
+//      atomics: order-free);
 //   2. per (b, h), an exclusive scan in (label, tile) order -> the first sorted position of
 //      each label inside each tile, and the cluster offsets;
 //   3. per tile, each token's rank among equal labels before it (wave ballots for the
-//      in-wave rank, an LDS prefix over the 16 waves) -> perm[pos] = token.
+//      in-wave rank, an LDS prefix over the tile's waves) -> perm[pos] = token.
 // Ties keep token order, so the result is the stable argsort.  Labels are masked to 8 bits,
 // so any input keeps every write inside perm.
 #include "vc_common.h"
 #include "vc_internal.h"
 
+template <int TILE>
 __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ labels, int N, int nblk,
                                                    int32_t* __restrict__ hist) {
   __shared__ int h[256];
@@ -19,8 +21,8 @@ __global__ __launch_bounds__(256) void k_sort_hist(const int32_t* __restrict__ l
   __syncthreads();
   const int32_t* lab = labels + (size_t)bh * N;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    int tok = blk * VC_SORT_TILE + r * 256 + t;
+  for (int r = 0; r < TILE / 256; ++r) {
+    int tok = blk * TILE + r * 256 + t;
     if (tok < N) atomicAdd(&h[lab[tok] & 255], 1);
   }
   __syncthreads();
@@ -60,14 +62,17 @@ __global__ __launch_bounds__(256) void k_sort_scan(int N, int nblk, int k, int32
   (void)N;
 }
 
-__global__ __launch_bounds__(1024) void k_sort_scatter(const int32_t* __restrict__ labels, int N, int nblk,
+// One thread per token of a TILE-token tile.
+template <int TILE>
+__global__ __launch_bounds__(TILE) void k_sort_scatter(const int32_t* __restrict__ labels, int N, int nblk,
                                                        const int32_t* __restrict__ base,
                                                        int32_t* __restrict__ perm) {
-  __shared__ int cnt[16][256];
+  constexpr int NW = TILE / 64;
+  __shared__ int cnt[NW][256];
   const int bh = blockIdx.y, blk = blockIdx.x, t = threadIdx.x;
   const int w = t >> 6, lane = t & 63;
-  for (int i = t; i < 16 * 256; i += 1024) (&cnt[0][0])[i] = 0;
-  const int tok = blk * VC_SORT_TILE + t;
+  for (int i = t; i < NW * 256; i += TILE) (&cnt[0][0])[i] = 0;
+  const int tok = blk * TILE + t;
   const bool valid = tok < N;
   const int lab = valid ? (labels[(size_t)bh * N + tok] & 255) : 0;
   // lanes of this wave holding the same label
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(1024) void k_sort_scatter(const int32_t* __restrict
   if (t < 256) {
     int run = 0;
 #pragma unroll
-    for (int ww = 0; ww < 16; ++ww) {
+    for (int ww = 0; ww < NW; ++ww) {
       int v = cnt[ww][t];
       cnt[ww][t] = run;
       run += v;
@@ -100,10 +105,20 @@ __global__ __launch_bounds__(1024) void k_sort_scatter(const int32_t* __restrict
 
 hipError_t vc_launch_label_sort(const int32_t* labels, int BH, int N, int k, int32_t* hist,
                                 int32_t* perm, int32_t* offsets, bool hist_ready, hipStream_t s) {
-  const int nblk = (N + VC_SORT_TILE - 1) / VC_SORT_TILE;
-  if (!hist_ready) hipLaunchKernelGGL(k_sort_hist, dim3(nblk, BH), dim3(256), 0, s, labels, N, nblk, hist);
+  const int tile = vc_group_tile(BH, N);
+  const int nblk = (N + tile - 1) / tile;
+  if (!hist_ready) {
+    if (tile == VC_SORT_TILE)
+      hipLaunchKernelGGL(k_sort_hist<VC_SORT_TILE>, dim3(nblk, BH), dim3(256), 0, s, labels, N, nblk, hist);
+    else
+      hipLaunchKernelGGL(k_sort_hist<VC_SORT_TILE_SMALL>, dim3(nblk, BH), dim3(256), 0, s, labels, N, nblk, hist);
+  }
   hipLaunchKernelGGL(k_sort_scan, dim3(BH), dim3(256), 0, s, N, nblk, k, hist, offsets);
-  hipLaunchKernelGGL(k_sort_scatter, dim3(nblk, BH), dim3(1024), 0, s, labels, N, nblk,
-                     (const int32_t*)hist, perm);
+  if (tile == VC_SORT_TILE)
+    hipLaunchKernelGGL(k_sort_scatter<VC_SORT_TILE>, dim3(nblk, BH), dim3(VC_SORT_TILE), 0, s, labels, N, nblk,
+                       (const int32_t*)hist, perm);
+  else
+    hipLaunchKernelGGL(k_sort_scatter<VC_SORT_TILE_SMALL>, dim3(nblk, BH), dim3(VC_SORT_TILE_SMALL), 0, s, labels,
+                       N, nblk, (const int32_t*)hist, perm);
   return hipGetLastError();
 }

@@ -27,10 +27,27 @@ struct vc_dq_ws {
 };
 vc_dq_ws vc_dq_ws_layout(int BH, int N);
 
-constexpr int VC_SORT_TILE = 1024;   // tokens per sort workgroup
+// Tokens per label-sort tile, which is also one k-means assign workgroup's share: 1024, or 256
+// when 1024-token tiles would give fewer than two workgroups per CU of the 256-CU chip (small
+// B*H*N), so that small shapes still spread over the chip.  A pure function of the shape, so
+// the workspace size and the launches agree.
+constexpr int VC_SORT_TILE = 1024;
+constexpr int VC_SORT_TILE_SMALL = 256;
+constexpr long long VC_SMALL_GRID = 512;
+inline int vc_group_tile(int BH, int N) {
+  const long long wg = (long long)BH * ((N + VC_SORT_TILE - 1) / VC_SORT_TILE);
+  return wg < VC_SMALL_GRID ? VC_SORT_TILE_SMALL : VC_SORT_TILE;
+}
 // VC_OK for hipSuccess, else VC_ERR_HIP with the error kept for vc_last_hip_error().
 int vc_hip_status(hipError_t e);
-constexpr int VC_KSTAT_CHUNK = 1024; // rows per key-mean partial
+// Rows per key-mean partial: 1024, or 256 for small shapes (the same rule).  The partials are
+// exact float64 sums of bf16 values, so the chunking does not change the mean.
+constexpr int VC_KSTAT_CHUNK = 1024;
+constexpr int VC_KSTAT_CHUNK_SMALL = 256;
+inline int vc_kstat_chunk(int BH, int N) {
+  const long long wg = (long long)BH * ((N + VC_KSTAT_CHUNK - 1) / VC_KSTAT_CHUNK);
+  return wg < VC_SMALL_GRID ? VC_KSTAT_CHUNK_SMALL : VC_KSTAT_CHUNK;
+}
 
 hipError_t vc_launch_test_expcast(const float* u, uint8_t* codes, size_t n, hipStream_t s);
 hipError_t vc_launch_test_e4m3(const float* x, uint8_t* codes, size_t n, hipStream_t s);
