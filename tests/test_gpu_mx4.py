@@ -123,7 +123,9 @@ def test_mx4_no_mean_flag():
     Kq4, sK4, Rq4, sR4, mu = _dev_ops(ops)
     O = values(bf16_host_bits(vc.vc_attn_fwd_mx4(bf16_dev(Q), Kq4, sK4, Rq4, sR4, None, no_mean=True)))
     rows = rows_sample(N, 512)
-    assert T.rel_l2(O[0, 0][rows], _emulated(ops[0], rows, mean=False)) < TOL
+    err = T.rel_l2(O[0, 0][rows], _emulated(ops[0], rows, mean=False))
+    note(f"  no mean: rel-L2 vs emulated = {err:.3e}")
+    assert err < TIGHT
 
 
 def test_mx4_end_to_end_and_vsmooth_gain():
@@ -166,7 +168,9 @@ def test_mx4_small_and_ragged_shapes():
                 vq = M.quantize_v4(Vh, perm[b, h])
                 ref = M.attention_tiled_mx4(M.dequant_row_groups(qc, qE), M.dequant_row_groups(kc, kE),
                                             M.dequant_v4(vq["codes"], vq["E"]), vq["mu_b"])
-                assert T.rel_l2(O[b, h], ref) < TOL
+                err = T.rel_l2(O[b, h], ref)
+                note(f"  b={b} h={h}: rel-L2 vs emulated = {err:.3e}")
+                assert err < TIGHT
 
 
 def test_mx4_empty_is_noop():

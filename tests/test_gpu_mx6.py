@@ -135,7 +135,9 @@ def test_mx6_no_mean_flag():
     Kq6, sK6, Rq6, sR6, mu = _dev_ops(ops)
     O = values(bf16_host_bits(vc.vc_attn_fwd_mx6(bf16_dev(Q), Kq6, sK6, Rq6, sR6, None, no_mean=True)))
     rows = rows_sample(N, 512)
-    assert T.rel_l2(O[0, 0][rows], _emulated(ops[0], rows, mean=False)) < TOL
+    err = T.rel_l2(O[0, 0][rows], _emulated(ops[0], rows, mean=False))
+    note(f"  no mean: rel-L2 vs emulated = {err:.3e}")
+    assert err < TIGHT
 
 
 def test_mx6_end_to_end_and_vsmooth_gain():
@@ -182,7 +184,9 @@ def test_mx6_small_and_ragged_shapes():
                 ref = M.attention_tiled_mx4(M.dequant_row_groups(ops["qc"], ops["qE"], FMT),
                                             M.dequant_row_groups(ops["kc"], ops["kE"], FMT),
                                             M.dequant_v4(ops["codes"], ops["E"], FMT), ops["mu_b"], fmt=FMT)
-                assert T.rel_l2(O[b, h], ref) < TOL
+                err = T.rel_l2(O[b, h], ref)
+                note(f"  b={b} h={h}: rel-L2 vs emulated = {err:.3e}")
+                assert err < TIGHT
 
 
 def test_mx6_empty_is_noop():
