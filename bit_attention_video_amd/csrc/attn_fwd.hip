@@ -462,6 +462,10 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
   // phase 2j+1 for step j-1 (K tile j+1, R tile j, first read in phase 2j+2).  Buffer reuse:
   // step j overwrites K tile j-1 and R tile j-2, whose last reads were in phase 2j-1.
   // A wave without queries only copies.
+  // The ExpCast loops run four steps per iteration: the copy ring is four deep, so every
+  // slot index inside the body is a constant.  The body is a macro because a lambda called
+  // there is not inlined and would put the loop state on the stack.  The exp-then-cast
+  // variant keeps the rolled loop, which allocates no scratch.
   if (!valid) {
     for (int j = 0; j < T; ++j) {
       issue(j);
@@ -478,13 +482,17 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     issue(0);
     vphase(0);
     wait_step();
-    for (int j = 1; j < T; ++j) {
-      mphase(j, Y, Y);
-      phase_barrier();
-      issue(j);
-      vphase(j);
-      wait_step();
-    }
+#define VC_STEP0(J) { mphase(J, Y, Y); phase_barrier(); issue(J); vphase(J); wait_step(); }
+    int j = 1;
+    if constexpr (!ETC)
+      for (; j + 3 < T; j += 4) {
+        VC_STEP0(j)
+        VC_STEP0(j + 1)
+        VC_STEP0(j + 2)
+        VC_STEP0(j + 3)
+      }
+    for (; j < T; ++j) VC_STEP0(j)
+#undef VC_STEP0
     mphase(T, X, Y);
     phase_barrier();
     wait_dma_barrier<0>();
@@ -493,13 +501,17 @@ __global__ __launch_bounds__(512) void k_attn_fwd(const uint16_t* __restrict__ Q
     phase_barrier();
     mphase(0, Y, X);
     wait_step();
-    for (int j = 1; j < T; ++j) {
-      issue(j);
-      vphase(j - 1);
-      phase_barrier();
-      mphase(j, Y, Y);
-      wait_step();
-    }
+#define VC_STEP1(J) { issue(J); vphase(J - 1); phase_barrier(); mphase(J, Y, Y); wait_step(); }
+    int j = 1;
+    if constexpr (!ETC)
+      for (; j + 3 < T; j += 4) {
+        VC_STEP1(j)
+        VC_STEP1(j + 1)
+        VC_STEP1(j + 2)
+        VC_STEP1(j + 3)
+      }
+    for (; j < T; ++j) VC_STEP1(j)
+#undef VC_STEP1
     vphase(T - 1);
     phase_barrier();
     mphase(T, X, Y);
