@@ -33,8 +33,10 @@ __device__ __forceinline__ int dq_token(const int32_t* perm, int bh, int N, int 
   return (unsigned)t < (unsigned)N ? t : 0;
 }
 
+// Four bf16 channels of a row, read with a streaming load: every pass of this file reads each
+// K or V row once (the two passes over a tensor are separate launches over all its rows).
 __device__ __forceinline__ void load4(const uint16_t* p, float* v) {
-  const uint2 raw = *(const uint2*)p;
+  const uint2 raw = ld_stream2(p);
   v[0] = bf16_to_f32(raw.x & 0xFFFFu);
   v[1] = bf16_to_f32(raw.x >> 16);
   v[2] = bf16_to_f32(raw.y & 0xFFFFu);
@@ -188,7 +190,7 @@ __device__ __forceinline__ void centred_quarter_row(const uint16_t* __restrict__
   if constexpr (!HAD) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const uint4 raw = src[v];
+      const uint4 raw = ld_stream4(src + v);
       const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
       const float4 k0 = *(const float4*)(kb + 8 * v), k1 = *(const float4*)(kb + 8 * v + 4);
       const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
@@ -203,7 +205,7 @@ __device__ __forceinline__ void centred_quarter_row(const uint16_t* __restrict__
   double y[32];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const uint4 raw = src[v];
+    const uint4 raw = ld_stream4(src + v);
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
     const float4 k0 = *(const float4*)(kb + 8 * v), k1 = *(const float4*)(kb + 8 * v + 4);
     const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V,
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int tok = dq_token(perm, bh, N, j * VC_BLK + rg + 8 * i);
-    raw[i] = *(const uint2*)(V + ((size_t)bh * N + tok) * VC_D + 4 * q4);
+    raw[i] = ld_stream2(V + ((size_t)bh * N + tok) * VC_D + 4 * q4);
   }
 #pragma unroll
   for (int i = 0; i < 16; ++i) *(uint2*)(vs + pv_slot(rg + 8 * i) * VC_D + 4 * q4) = raw[i];

@@ -14,6 +14,20 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 
+// Streaming loads for data a kernel reads once (the bf16 K and V rows of the preprocessing passes):
+// nontemporal, so the lines are not kept in the caches for reuse that never comes.  On MI355X a
+// read-only stream of this form sustains about 6 TB/s against about 5.4 TB/s for plain loads.
+__device__ __forceinline__ uint2 ld_stream2(const void* p) {
+  typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+  const v2u v = __builtin_nontemporal_load((const v2u*)p);
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ uint4 ld_stream4(const void* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load((const v4u*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // bf16 bit pattern -> float32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
