@@ -19,17 +19,19 @@ __device__ __forceinline__ float pair_max(float x) {
 // is awaited explicitly (vmcnt) before the barrier that publishes a tile.
 // The global address is a per-lane 64-bit VGPR address.  (An SGPR base would need the five
 // wait states gfx9 requires between a vector write of an SGPR and a memory instruction that
-// reads it, which the compiler does not insert in front of inline assembly.)  The compiler
-// writes M0 for the "{m0}" operand; the s_nop 4 in front of the copy gives five wait states,
-// enough for the strictest case (M0 written by a vector instruction such as v_readfirstlane;
-// a scalar write needs one), so the guard does not depend on how M0 was produced.
+// reads it, which the compiler does not insert in front of inline assembly.)  M0 is written
+// inside the same asm block by s_mov_b32 from a scalar operand, so it is always a scalar write,
+// which needs one wait state before the copy reads M0 (the s_nop 0), whatever code produced the
+// operand.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
   const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+               : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds_base) {
   const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds_base) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
+               : "memory", "m0");
 }
 // Workgroup barrier between two phases.  No LDS read needs to be complete here: every tile
 // buffer is rewritten only after the instructions that consume its reads, and the compiler
