@@ -17,21 +17,29 @@ __device__ __forceinline__ float pair_max(float x) {
 // assembly on purpose: the compiler cannot tell the tile being filled from the tiles being
 // read, and would otherwise wait for every prefetch before the next LDS read.  Completion
 // is awaited explicitly (vmcnt) before the barrier that publishes a tile.
-// The global address is a per-lane 64-bit VGPR address.  (An SGPR base would need the five
-// wait states gfx9 requires between a vector write of an SGPR and a memory instruction that
-// reads it, which the compiler does not insert in front of inline assembly.)  M0 is written
-// inside the same asm block by s_mov_b32 from a scalar operand, so it is always a scalar write,
-// which needs one wait state before the copy reads M0 (the s_nop 0), whatever code produced the
-// operand.
+// M0 is written inside the same asm block by s_mov_b32 from a scalar operand, so it is always a
+// scalar write, which needs one wait state before the copy reads M0 (the s_nop 0), whatever
+// code produced the operand.  (M0 is not in the clobber lists: the compiler treats it as a
+// reserved register and keeps no value in it across these kernels, whose only M0 uses are these
+// copies.)
+// The global address is a scalar base plus a per-lane 32-bit offset, so a copy costs no vector
+// instruction.  The base is first moved by s_mov_b64 into a scalar pair of the asm block's own,
+// so the copy reads an SGPR pair written by a scalar instruction, which needs no wait states; a
+// base written by a vector instruction (v_readfirstlane) would need five before a memory
+// instruction reads it, and the compiler does not insert them in front of inline assembly.
 __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
-               : "memory", "m0");
+  uint64_t base;
+  asm volatile("s_mov_b64 %0, %2\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %0"
+               : "=&s"(base)
+               : "v"(voff), "s"(gbase), "s"(lds_base)
+               : "memory");
 }
 __device__ __forceinline__ void dma4(const void* gbase, uint32_t voff, uint32_t lds_base) {
-  const uint8_t* g = (const uint8_t*)gbase + voff;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base)
-               : "memory", "m0");
+  uint64_t base;
+  asm volatile("s_mov_b64 %0, %2\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\tglobal_load_lds_dword %1, %0"
+               : "=&s"(base)
+               : "v"(voff), "s"(gbase), "s"(lds_base)
+               : "memory");
 }
 // Workgroup barrier between two phases.  No LDS read needs to be complete here: every tile
 // buffer is rewritten only after the instructions that consume its reads, and the compiler

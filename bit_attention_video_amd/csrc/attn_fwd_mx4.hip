@@ -235,14 +235,7 @@ __global__ __launch_bounds__(512) void k_attn_fwd_mx4(const uint16_t* __restrict
   const uint32_t mr0 = lds_addr(&mring[0][0]);
   constexpr int D = NBUF - 1;
   auto clampT = [&](int i) { return i < T ? i : T - 1; };
-  // the 4-byte copies' lane offset; at 6 bits made opaque at each use, so the compiler adds it
-  // to the tile address per copy instead of keeping a 64-bit per-lane address live across the
-  // loop (which the 6-bit register budget would spill)
-  auto lane4 = [&]() {
-    uint32_t o = 4 * lane;
-    if constexpr (BITS == 6) asm volatile("" : "+v"(o));
-    return o;
-  };
+  auto lane4 = [&]() { return (uint32_t)(4 * lane); };   // the 4-byte copies' lane offset
   auto k_tile = [&](int i, int slot) {
     dma16(Kh + (size_t)i * TILE4, so, kt0 + slot * TILE4);
     if constexpr (NC == 2) dma16(Kh + (size_t)i * TILE4, so1, kt0 + slot * TILE4 + 1024);
