@@ -190,7 +190,7 @@ __device__ __forceinline__ void centred_quarter_row(const uint16_t* __restrict__
   if constexpr (!HAD) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      const uint4 raw = ld_stream4(src + v);
+      const uint4 raw = src[v];
       const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
       const float4 k0 = *(const float4*)(kb + 8 * v), k1 = *(const float4*)(kb + 8 * v + 4);
       const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
@@ -205,7 +205,7 @@ __device__ __forceinline__ void centred_quarter_row(const uint16_t* __restrict__
   double y[32];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const uint4 raw = ld_stream4(src + v);
+    const uint4 raw = src[v];
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
     const float4 k0 = *(const float4*)(kb + 8 * v), k1 = *(const float4*)(kb + 8 * v + 4);
     const float kk[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
