@@ -26,6 +26,9 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # score with vector instructions, and AGPR copies would double that traffic
           "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-result"]
+# Sources built at another optimisation level than CFLAGS': the rotated no-mean 6-bit attention
+# instantiation gives wrong outputs on the device when built at -O3 and matches the reference at -O2.
+OPT_LEVEL = {"attn_fwd_mx6_rn.hip": "-O2"}
 
 
 def hipcc() -> str:
@@ -41,7 +44,8 @@ def sources():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", src, "-o", obj]
+    flags = [OPT_LEVEL.get(os.path.basename(src), f) if f == "-O3" else f for f in CFLAGS]
+    cmd = [hipcc(), *flags, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

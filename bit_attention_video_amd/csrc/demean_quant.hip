@@ -20,7 +20,7 @@
 //                    PV operand order;
 //                    mu~ = bf16(mu / sV)
 //   k_kquant4, k_vquant4   the 4-bit path's K and V operands (MX E2M1, per-32 scales)
-//   k_kquant6, k_vquant6   the 6-bit path's (MX E2M3, per-32 scales, 32-byte groups)
+//   k_kquant6, k_vquant6   the 6-bit path's (MX E2M3, per-32 scales, 128-byte rows of four groups)
 #include "vc_common.h"
 #include "vc_internal.h"
 #include "vc_attn.h"
@@ -533,10 +533,20 @@ __global__ __launch_bounds__(256) void k_vquant4(const uint16_t* __restrict__ V,
   if (t < VC_D) ((uint32_t*)(sR4 + ((size_t)bh * nt + j) * (VC_D * 4)))[t] = ((const uint32_t*)stile)[t];
 }
 
+// Group g (0..3) of a 6-bit row of 128 bytes: its first 16 code bytes at 16 g, its last 8 at
+// 64 + 16 (g % 2) + 8 (g / 2) (groups 0 and 2 share chunk 4, groups 1 and 3 chunk 5, so an
+// attention lane reads the tails of both its groups in one 16-byte read), and 8 of the row's 32
+// trailing zero bytes at 96 + 8 g.
+__device__ __forceinline__ void fp6_row_store(uint8_t* row, int g, const v6i& w) {
+  *(uint4*)(row + 16 * g) = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
+  *(uint2*)(row + 64 + 16 * (g & 1) + 8 * (g >> 1)) = make_uint2((uint32_t)w[4], (uint32_t)w[5]);
+  *(uint2*)(row + 96 + 8 * g) = make_uint2(0u, 0u);
+}
+
 // 6-bit K (MX E2M3): four lanes per permuted row, lane (row, c4) quantising channels
 // 32 c4 .. 32 c4 + 31, one scale group: its own maximum, E = mx6_exponent, codes of z / 2^E
-// (exact division) packed into 24 bytes, then 8 zero bytes, so a row is four 32-byte groups
-// (the layout the 6-bit attention's fragments read).  With HAD the row is rotated first and the
+// (exact division) packed into 24 bytes and stored as group c4 of the row (fp6_row_store, the
+// layout the 6-bit attention's fragments read).  With HAD the row is rotated first and the
 // stored exponent lowered by 7 (the 1/128 of H / 128).
 template <bool HAD>
 __global__ __launch_bounds__(512) void k_kquant6(const uint16_t* __restrict__ K, const int32_t* __restrict__ perm,
@@ -556,9 +566,7 @@ __global__ __launch_bounds__(512) void k_kquant6(const uint16_t* __restrict__ K,
   for (int k = 0; k < 32; ++k) z[k] *= inv;
   const v6i w = fp6x32(z);
   const size_t r = (size_t)bh * N + j * VC_BLK + row;
-  uint4* dst = (uint4*)(Kq6 + r * VC_D + 32 * c4);
-  dst[0] = make_uint4((uint32_t)w[0], (uint32_t)w[1], (uint32_t)w[2], (uint32_t)w[3]);
-  dst[1] = make_uint4((uint32_t)w[4], (uint32_t)w[5], 0u, 0u);
+  fp6_row_store(Kq6 + r * VC_D, c4, w);
   sK6[r * 4 + c4] = (uint8_t)(E - (HAD ? 7 : 0) + 127);
 }
 
@@ -571,8 +579,8 @@ __device__ __forceinline__ int pv_slot(int r) {
 // 6-bit V residual (MX E2M3), per tile j: the gathered rows V'[pi] staged in LDS as bf16 in
 // slot order [slot][channel] (a thread copies four channels of one row); then thread
 // (channel pair, group) takes the 32 slots of its group for both channels, R = V' - mu_j in
-// float32, each channel's maximum and scale, and writes its two 24-code-byte groups (plus 8 zero
-// bytes each) to [channel][32 g] of the tile-transposed operand; scale bytes [channel][group];
+// float32, each channel's maximum and scale, and writes its two 24-code-byte groups into the
+// channels' 128-byte rows of the tile-transposed operand (fp6_row_store); scale bytes [channel][group];
 // mu_out = bf16(mu_j), unscaled.
 constexpr int V6_OROW = 144;   // LDS bytes per channel row of the 6-bit output tile (128 + pad)
 
@@ -624,12 +632,8 @@ __global__ __launch_bounds__(256) void k_vquant6(const uint16_t* __restrict__ V,
   // 16 KB copy rather than 32-byte pieces of 128 rows
   __syncthreads();   // every read of vs is done
   uint8_t* ot = (uint8_t*)vs;
-  uint4* d0 = (uint4*)(ot + (2 * c2) * V6_OROW + 32 * g);
-  uint4* d1 = (uint4*)(ot + (2 * c2 + 1) * V6_OROW + 32 * g);
-  d0[0] = make_uint4((uint32_t)w0[0], (uint32_t)w0[1], (uint32_t)w0[2], (uint32_t)w0[3]);
-  d0[1] = make_uint4((uint32_t)w0[4], (uint32_t)w0[5], 0u, 0u);
-  d1[0] = make_uint4((uint32_t)w1[0], (uint32_t)w1[1], (uint32_t)w1[2], (uint32_t)w1[3]);
-  d1[1] = make_uint4((uint32_t)w1[4], (uint32_t)w1[5], 0u, 0u);
+  fp6_row_store(ot + (2 * c2) * V6_OROW, g, w0);
+  fp6_row_store(ot + (2 * c2 + 1) * V6_OROW, g, w1);
   uint8_t* sc = (uint8_t*)(ot + VC_D * V6_OROW);
   sc[(2 * c2) * 4 + g] = (uint8_t)(E0 + 127);
   sc[(2 * c2 + 1) * 4 + g] = (uint8_t)(E1 + 127);

@@ -93,6 +93,10 @@ hipError_t vc_launch_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const u
                                   const uint8_t* Rq4, const uint8_t* sR4, const uint16_t* mu,
                                   int BH, int N, float L4, unsigned flags, uint16_t* O,
                                   int bits, hipStream_t s);  // L4 = float32(log2(e) softmax_scale)
+// The 6-bit kernel with VC_ATTN_NO_MEAN | VC_ATTN_HADAMARD (built at -O2, attn_fwd_mx6_rn.hip).
+hipError_t vc_launch_attn_fwd_mx6_rn(const uint16_t* Q, const uint8_t* Kq6, const uint8_t* sK6,
+                                     const uint8_t* Rq6, const uint8_t* sR6, const uint16_t* mu, int BH, int N, float L4,
+                                     uint16_t* O, hipStream_t s);
 
 // clk: NULL, or 4 x vc_attn_fwd_workgroups(BH, N) uint64 that receive each workgroup's start
 // and end stamps (shader cycles, constant-rate ticks) for the clock probe.

@@ -256,8 +256,11 @@ int vc_attn_fwd_mx4(const uint16_t* Q, const uint8_t* Kq4, const uint8_t* sK4, c
  * E2M3: sign, 2-bit exponent (bias 1), 3-bit mantissa; magnitudes m/8 (m < 8), then 1 to 1.875,
  * 2 to 3.75, 4 to 7.5 in steps of 1/8, 1/4, 1/2.  Group scale 2^E: the smallest power of two
  * with amax <= 7.5 * 2^E (E >= -100, E = 0 for an all-zero group), stored as the byte E + 127;
- * elements E2M3_RNE(x / 2^E).  A group of 32 elements is 32 bytes: 24 code bytes, element k in
- * bits 6k .. 6k + 5 of the 192-bit little-endian field, then 8 zero bytes.
+ * elements E2M3_RNE(x / 2^E).  A group of 32 elements has 24 code bytes, element k in bits
+ * 6k .. 6k + 5 of its 192-bit little-endian field.  The four groups of a 128-byte operand row are
+ * stored with the first 16 code bytes of group g at byte 16 g and its last 8 at byte
+ * 64 + 16 (g % 2) + 8 (g / 2) (the last 8 of groups 0 and 2 in bytes 64 .. 79, of groups 1 and 3
+ * in bytes 80 .. 95); bytes 96 .. 127 are zero.
  *
  * vc_vsmooth_demean_quant_mx6: as vc_vsmooth_demean_quant_mx4, with
  *   Kq6 [B,H,N,128]: the four 32-channel groups of each permuted row; sK6 [B,H,N,4];

@@ -170,12 +170,15 @@ def test_fp6_pack_roundtrip_and_layout():
     rng = np.random.default_rng(5)
     c = rng.integers(0, 64, (2, 3, 128)).astype(np.uint8)
     p = vc.pack_fp6(c)
-    assert p.shape == c.shape and not p.reshape(-1, 32)[:, 24:].any()
+    assert p.shape == c.shape and not p.reshape(-1, 128)[:, 96:].any()   # 32 zero bytes per row
     assert np.array_equal(vc.unpack_fp6(p), c)
+    # group g of a row: its first 16 code bytes at 16 g, its last 8 at 64 + 16 (g % 2) + 8 (g // 2);
     # value k in bits 6k .. 6k+5 of the group's little-endian 192-bit field
-    g = p.reshape(-1, 32)[0, :24]
-    field = int.from_bytes(bytes(g.tolist()), "little")
-    assert [(field >> (6 * k)) & 63 for k in range(32)] == c.reshape(-1, 32)[0].tolist()
+    row = p.reshape(-1, 128)[0]
+    for g in range(4):
+        t = 64 + 16 * (g % 2) + 8 * (g // 2)
+        field = int.from_bytes(bytes(row[16 * g:16 * g + 16].tolist() + row[t:t + 8].tolist()), "little")
+        assert [(field >> (6 * k)) & 63 for k in range(32)] == c.reshape(-1, 32)[g].tolist()
 
 
 def test_fp4_pack_roundtrip():

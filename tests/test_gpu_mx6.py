@@ -68,7 +68,7 @@ def test_mx6_quantisers_bit_exact(name, heads, perm_kind, no_demean, had):
                                          no_demean=no_demean, hadamard=had)
     kraw = ops["Kq6"].cpu().numpy()
     rraw = ops["Rq6"].cpu().numpy()
-    assert not kraw.reshape(-1, 32)[:, 24:].any() and not rraw.reshape(-1, 32)[:, 24:].any()   # pad bytes
+    assert not kraw.reshape(-1, 128)[:, 96:].any() and not rraw.reshape(-1, 128)[:, 96:].any()   # pad bytes
     kc_g = vc.unpack_fp6(kraw)
     sk_g = ops["sK6"].cpu().numpy().astype(np.int64) - 127
     rc_g = vc.rq_tiled_to_natural(torch.from_numpy(vc.unpack_fp6(rraw))).numpy()
@@ -127,17 +127,23 @@ def test_mx6_attention_on_oracle_operands(name, heads, nrows, had):
         assert err < (TOL if had else TIGHT)
 
 
-def test_mx6_no_mean_flag():
-    cfg, Q, K, V = config_inputs("medium", [4])
+@pytest.mark.parametrize("name,heads,had", [("medium", [4], False), ("medium", [4], True),
+                                           ("qk_outlier", [2], True), ("video", [7], True)])
+def test_mx6_no_mean_flag(name, heads, had):
+    """Without the mean term, plain and rotated: the rotated no-mean kernel is the one built at -O2
+    (its -O3 code gave wrong outputs)."""
+    cfg, Q, K, V = config_inputs(name, heads)
+    note(f"mx6 no-mean {name} heads={heads} hadamard={had}")
     N = cfg.N
     perm = _perm("random", N, 1, 3)
-    ops = [_oracle_ops(values(Q[0, 0]), values(K[0, 0]), values(V[0, 0]), perm[0, 0])]
+    ops = [_oracle_ops(values(Q[0, 0]), values(K[0, 0]), values(V[0, 0]), perm[0, 0], had)]
     Kq6, sK6, Rq6, sR6, mu = _dev_ops(ops)
-    O = values(bf16_host_bits(vc.vc_attn_fwd_mx6(bf16_dev(Q), Kq6, sK6, Rq6, sR6, None, no_mean=True)))
-    rows = rows_sample(N, 512)
+    O = values(bf16_host_bits(vc.vc_attn_fwd_mx6(bf16_dev(Q), Kq6, sK6, Rq6, sR6, None, no_mean=True,
+                                                 hadamard=had)))
+    rows = rows_sample(N, 512 if N <= 8192 else 256)
     err = T.rel_l2(O[0, 0][rows], _emulated(ops[0], rows, mean=False))
     note(f"  no mean: rel-L2 vs emulated = {err:.3e}")
-    assert err < TIGHT
+    assert err < (TOL if had else TIGHT)
 
 
 def test_mx6_end_to_end_and_vsmooth_gain():
