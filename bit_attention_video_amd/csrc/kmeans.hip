@@ -63,8 +63,13 @@ __global__ __launch_bounds__(128) void k_kmeans_prep(const float* __restrict__ C
   }
 }
 
-// TOK tokens per workgroup (8 waves x TOK/256 groups x 32): one label-sort tile.
-template <int TOK>
+// TOK tokens per workgroup (8 waves x TOK/(256 NSET) groups x NSET sets of 32): one label-sort tile.
+// The 1024-token tile takes two sets per wave without prefetch: each centroid fragment read from
+// LDS then feeds two products, and the kernel keeps four waves per SIMD (126 registers).  One set
+// with the next group prefetched reads twice the LDS bytes per token; two sets with prefetch need
+// 194 registers (two waves per SIMD), and four sets 220; at the video and long sizes the chosen
+// form is 2-4 % faster over the whole grouping than either, with the same labels.
+template <int TOK, int NSET, bool PF>
 __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restrict__ V,
                                                        const uint16_t* __restrict__ phi,
                                                        const uint16_t* __restrict__ plo,
@@ -91,115 +96,158 @@ __global__ __launch_bounds__(512) void k_kmeans_assign(const uint16_t* __restric
   if (t < 256) hcount[t] = 0;
   __syncthreads();
 
-  // Each wave takes 32 tokens per group (lane (q, g): token q, channel half g of every
-  // 16-channel chunk); the rows of the next group are loaded while the current one is
-  // computed.  Token indices past N are clamped (their labels are not written).
+  // Each wave takes NSET sets of 32 tokens per group (lane (q, g): token q of every set, channel
+  // half g of every 16-channel chunk); with PF the rows of the next group are loaded while the
+  // current one is computed.  Token indices past N are clamped (their labels are not written).
+  constexpr int SET = KM_THREADS / 2, NG = TOK / (SET * NSET);
   const int w = t >> 6, lane = t & 63, q = lane & 31, g = lane >> 5;
   const int nblk = kpad >> 5;
   const uint16_t* Vb = V + (size_t)bh * N * VC_D + 8 * g;
-  auto tok_of = [&](int grp) { return blockIdx.x * TOK + grp * (KM_THREADS / 2) + w * 32 + q; };
-  auto load_rows = [&](int grp, v8s (&vb)[8]) {
-    const int tok = tok_of(grp);
-    const uint16_t* vrow = Vb + (size_t)(tok < N ? tok : N - 1) * VC_D;
+  auto tok_of = [&](int grp, int u) { return blockIdx.x * TOK + (grp * NSET + u) * SET + w * 32 + q; };
+  auto load_rows = [&](int grp, v8s (&vb)[NSET][8]) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) vb[c] = __builtin_bit_cast(v8s, *(const uint4*)(vrow + 16 * c));
+    for (int u = 0; u < NSET; ++u) {
+      const int tok = tok_of(grp, u);
+      const uint16_t* vrow = Vb + (size_t)(tok < N ? tok : N - 1) * VC_D;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) vb[u][c] = __builtin_bit_cast(v8s, *(const uint4*)(vrow + 16 * c));
+    }
   };
-  v8s vcur[8], vnext[8];
+  // Block cb's accumulator starts from -||c||^2 / 2 of this lane's 16 candidates,
+  // ci = 32 cb + 8 m + 4 g + r in element 4 m + r.
+  auto init = [&](int cb) {
+    v16f a;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float4 n4 = *(const float4*)(cn + cb * 32 + 8 * m + 4 * g);
+      a[4 * m + 0] = n4.x; a[4 * m + 1] = n4.y; a[4 * m + 2] = n4.z; a[4 * m + 3] = n4.w;
+    }
+    return a;
+  };
+  auto frag = [&](const uint16_t* tab, int cb, int c) {
+    return __builtin_bit_cast(v8bf, *(const v8s*)(tab + (cb * 32 + q) * KM_ROW + 8 * g + 16 * c));
+  };
+  // The best of a block's 16 candidates by a depth-4 tree in which the higher-index side wins
+  // only when strictly larger: the maximum, and among equal maxima the lowest candidate, as a
+  // scan in index order finds (for finite distances).  Then merged into the running best,
+  // the blocks taken in index order.
+  auto block_best = [&](const v16f& a, int cb, float& best, int& bi) {
+    float v[8];
+    int e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool gt = a[2 * i + 1] > a[2 * i];
+      v[i] = gt ? a[2 * i + 1] : a[2 * i];
+      e[i] = gt ? 2 * i + 1 : 2 * i;
+    }
+#pragma unroll
+    for (int n = 4; n >= 1; n >>= 1)
+#pragma unroll
+      for (int i = 0; i < n; ++i) {
+        const bool gt = v[2 * i + 1] > v[2 * i];
+        v[i] = gt ? v[2 * i + 1] : v[2 * i];
+        e[i] = gt ? e[2 * i + 1] : e[2 * i];
+      }
+    if (v[0] > best) {
+      best = v[0];
+      bi = cb * 32 + 4 * g + e[0] + 4 * (e[0] >> 2);   // element 4 m + r -> 8 m + 4 g + r
+    }
+  };
+  v8s vcur[NSET][8], vnext[PF ? NSET : 1][8];
   load_rows(0, vcur);
 #pragma unroll
-  for (int grp = 0; grp < TOK / (KM_THREADS / 2); ++grp) {
-    if (grp + 1 < TOK / (KM_THREADS / 2)) load_rows(grp + 1, vnext);
-    float best = -__builtin_inff();   // max of v.c - ||c||^2 / 2
-    int bi = 0;
-    // Block cb's accumulator starts from -||c||^2 / 2 of this lane's 16 candidates,
-    // ci = 32 cb + 8 m + 4 g + r in element 4 m + r.
-    auto init = [&](int cb) {
-      v16f a;
+  for (int grp = 0; grp < NG; ++grp) {
+    if constexpr (PF)
+      if (grp + 1 < NG) load_rows(grp + 1, vnext);
+    float best[NSET];   // max of v.c - ||c||^2 / 2
+    int bi[NSET];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float4 n4 = *(const float4*)(cn + cb * 32 + 8 * m + 4 * g);
-        a[4 * m + 0] = n4.x; a[4 * m + 1] = n4.y; a[4 * m + 2] = n4.z; a[4 * m + 3] = n4.w;
-      }
-      return a;
-    };
-    auto frag = [&](const uint16_t* tab, int cb, int c) {
-      return __builtin_bit_cast(v8bf, *(const v8s*)(tab + (cb * 32 + q) * KM_ROW + 8 * g + 16 * c));
-    };
-    // The best of a block's 16 candidates by a depth-4 tree in which the higher-index side wins
-    // only when strictly larger: the maximum, and among equal maxima the lowest candidate, as a
-    // scan in index order finds (for finite distances).  Then merged into the running best,
-    // the blocks taken in index order.
-    auto block_best = [&](const v16f& a, int cb) {
-      float v[8];
-      int e[8];
+    for (int u = 0; u < NSET; ++u) { best[u] = -__builtin_inff(); bi[u] = 0; }
+    // Each block's own sum runs in the same order (-||c||^2/2, then hi and lo of chunk 0, hi and
+    // lo of chunk 1, ...).  With one set, two blocks at a time: their product chains are
+    // independent, so the matrix unit never waits for the previous product of the same chain;
+    // with two sets, the sets' chains are the independent pair and each centroid fragment read
+    // from LDS feeds both.
+    if constexpr (NSET == 1) {
+      int cb = 0;
+      for (; cb + 1 < nblk; cb += 2) {
+        v16f a0 = init(cb), a1 = init(cb + 1);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const bool gt = a[2 * i + 1] > a[2 * i];
-        v[i] = gt ? a[2 * i + 1] : a[2 * i];
-        e[i] = gt ? 2 * i + 1 : 2 * i;
-      }
-#pragma unroll
-      for (int n = 4; n >= 1; n >>= 1)
-#pragma unroll
-        for (int i = 0; i < n; ++i) {
-          const bool gt = v[2 * i + 1] > v[2 * i];
-          v[i] = gt ? v[2 * i + 1] : v[2 * i];
-          e[i] = gt ? e[2 * i + 1] : e[2 * i];
+        for (int c = 0; c < 8; ++c) {
+          const v8bf b = __builtin_bit_cast(v8bf, vcur[0][c]);
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb, c), b, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb + 1, c), b, a1, 0, 0, 0);
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb, c), b, a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb + 1, c), b, a1, 0, 0, 0);
         }
-      if (v[0] > best) {
-        best = v[0];
-        bi = cb * 32 + 4 * g + e[0] + 4 * (e[0] >> 2);   // element 4 m + r -> 8 m + 4 g + r
+        block_best(a0, cb, best[0], bi[0]);
+        block_best(a1, cb + 1, best[0], bi[0]);
       }
-    };
-    // Two blocks at a time: their product chains are independent, so the matrix unit never waits
-    // for the previous product of the same chain.  Each block's own sum runs in the same order
-    // (-||c||^2/2, then hi and lo of chunk 0, hi and lo of chunk 1, ...).
-    int cb = 0;
-    for (; cb + 1 < nblk; cb += 2) {
-      v16f a0 = init(cb), a1 = init(cb + 1);
+      if (cb < nblk) {   // an odd last block (uniform)
+        v16f a0 = init(cb);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const v8bf b = __builtin_bit_cast(v8bf, vcur[c]);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb, c), b, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb + 1, c), b, a1, 0, 0, 0);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb, c), b, a0, 0, 0, 0);
-        a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb + 1, c), b, a1, 0, 0, 0);
-      }
-      block_best(a0, cb);
-      block_best(a1, cb + 1);
-    }
-    if (cb < nblk) {   // an odd last block (uniform)
-      v16f a0 = init(cb);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const v8bf b = __builtin_bit_cast(v8bf, vcur[c]);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb, c), b, a0, 0, 0, 0);
-        a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb, c), b, a0, 0, 0, 0);
-      }
-      block_best(a0, cb);
-    }
-    const float ob = __shfl_xor(best, 32, 64);
-    const int oi = __shfl_xor(bi, 32, 64);
-    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
-    const int tok = tok_of(grp);
-    if (tok < N && g == 0) {
-      labels[(size_t)bh * N + tok] = bi;
-      if (hist) atomicAdd(&hcount[bi & 255], 1);   // integer counts: order-free
-    }
-    if (mindist) {   // ||v||^2 - 2 (v.c - ||c||^2 / 2) of the winner (test output only)
-      float vn = 0.0f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = bf16_to_f32((uint16_t)vcur[c][e]);
-          vn = fmaf(x, x, vn);
+        for (int c = 0; c < 8; ++c) {
+          const v8bf b = __builtin_bit_cast(v8bf, vcur[0][c]);
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(chi, cb, c), b, a0, 0, 0, 0);
+          a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag(clo, cb, c), b, a0, 0, 0, 0);
         }
-      vn += __shfl_xor(vn, 32, 64);
-      if (tok < N && g == 0) mindist[(size_t)bh * N + tok] = fmaf(-2.0f, best, vn);
+        block_best(a0, cb, best[0], bi[0]);
+      }
+    } else {
+      for (int cb = 0; cb < nblk; ++cb) {
+        v16f a[NSET];
+        a[0] = init(cb);
+#pragma unroll
+        for (int u = 1; u < NSET; ++u) a[u] = a[0];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const v8bf fh = frag(chi, cb, c), fl = frag(clo, cb, c);
+#pragma unroll
+          for (int u = 0; u < NSET; ++u)
+            a[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fh, __builtin_bit_cast(v8bf, vcur[u][c]), a[u], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < NSET; ++u)
+            a[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fl, __builtin_bit_cast(v8bf, vcur[u][c]), a[u], 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < NSET; ++u) block_best(a[u], cb, best[u], bi[u]);
+      }
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c) vcur[c] = vnext[c];
+    for (int u = 0; u < NSET; ++u) {
+      float bu = best[u];
+      int iu = bi[u];
+      const float ob = __shfl_xor(bu, 32, 64);
+      const int oi = __shfl_xor(iu, 32, 64);
+      if (ob > bu || (ob == bu && oi < iu)) { bu = ob; iu = oi; }
+      const int tok = tok_of(grp, u);
+      if (tok < N && g == 0) {
+        labels[(size_t)bh * N + tok] = iu;
+        if (hist) atomicAdd(&hcount[iu & 255], 1);   // integer counts: order-free
+      }
+      if (mindist) {   // ||v||^2 - 2 (v.c - ||c||^2 / 2) of the winner (test output only)
+        float vn = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float x = bf16_to_f32((uint16_t)vcur[u][c][e]);
+            vn = fmaf(x, x, vn);
+          }
+        vn += __shfl_xor(vn, 32, 64);
+        if (tok < N && g == 0) mindist[(size_t)bh * N + tok] = fmaf(-2.0f, bu, vn);
+      }
+    }
+    if (grp + 1 < NG) {
+      if constexpr (PF) {
+#pragma unroll
+        for (int u = 0; u < NSET; ++u)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) vcur[u][c] = vnext[u][c];
+      } else {
+        load_rows(grp + 1, vcur);
+      }
+    }
   }
   if (hist) {   // a workgroup's TOK tokens are one tile of the label sort
     __syncthreads();
@@ -331,10 +379,10 @@ static hipError_t assign_lds_limit() {
   const unsigned long long bit = dev < 64 ? (1ull << dev) : 0ull;
   if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
   const size_t lds_max = (size_t)2 * VC_MAX_K * KM_ROW * sizeof(uint16_t) + (size_t)VC_MAX_K * sizeof(float);
-  e = hipFuncSetAttribute((const void*)k_kmeans_assign<VC_SORT_TILE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  e = hipFuncSetAttribute((const void*)k_kmeans_assign<VC_SORT_TILE, 2, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           (int)lds_max);
   if (e == hipSuccess)
-    e = hipFuncSetAttribute((const void*)k_kmeans_assign<VC_SORT_TILE_SMALL>,
+    e = hipFuncSetAttribute((const void*)k_kmeans_assign<VC_SORT_TILE_SMALL, 1, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
   if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
   return e;
@@ -351,10 +399,10 @@ hipError_t vc_launch_kmeans_assign(const uint16_t* V, const float* C, int BH, in
   const int tile = vc_group_tile(BH, N);   // the label sort's tile, whose histograms hist holds
   const int nblk = (N + tile - 1) / tile;
   if (tile == VC_SORT_TILE)
-    hipLaunchKernelGGL(k_kmeans_assign<VC_SORT_TILE>, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V,
+    hipLaunchKernelGGL((k_kmeans_assign<VC_SORT_TILE, 2, false>), dim3(nblk, BH), dim3(KM_THREADS), lds, s, V,
                        (const uint16_t*)chi, (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist, hist);
   else
-    hipLaunchKernelGGL(k_kmeans_assign<VC_SORT_TILE_SMALL>, dim3(nblk, BH), dim3(KM_THREADS), lds, s, V,
+    hipLaunchKernelGGL((k_kmeans_assign<VC_SORT_TILE_SMALL, 1, true>), dim3(nblk, BH), dim3(KM_THREADS), lds, s, V,
                        (const uint16_t*)chi, (const uint16_t*)clo, (const float*)cn, N, kpad, labels, mindist, hist);
   return hipGetLastError();
 }
