@@ -1,6 +1,6 @@
 // The 4-bit and 6-bit VC-Attention forward kernel on gfx950 (a header: the rotated no-mean
 // 6-bit instantiation is built in a translation unit of its own, attn_fwd_mx6_rn.hip).
-// 4-bit operands: MX E2M1 operands under per-32 E8M0 scales for Q, K, P
+// At 4 bits the operands are MX E2M1 under per-32 E8M0 scales for Q, K, P
 // and the value residual (VC-Attention Sec. 3.2 Eq. 4 and Eq. 6 with the 4-bit value quantiser;
 // Sec. 4.1 "Implementation"; App. A "Scope of ExpCast-FP8"; App. B).
 //
